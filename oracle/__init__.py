@@ -1,0 +1,50 @@
+"""CPU oracle for exact scaled-dot-product attention (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path imports, calls or links
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it. It shares no code, table or
+helper with the HIP library; the only thing both sides share is the seeded
+input generator in ``synth``.
+
+Pages cited (by title and section):
+
+* [BLOG] "AI infra. 一层全看懂(五)Flash Attention:AI编译优化的集大成者"
+  (yeyulingfeng.com): §一 the three steps QK^T -> softmax -> PV; §三 the
+  standard three-pass attention with its FLOP and byte counts; §四 safe
+  softmax (subtract the row maximum) and the tiling notation B_r, B_c.
+* [KB] "FlashAttention：为什么少搬数据，反而算得更快" (xuujii.github.io ai-infra-kb,
+  M007): §02 the three actions and the note that scale and causal mask are
+  part of the real computation; §04 the online-softmax state (m, l, U), its
+  update rule, the initial state and the hand-worked example; §05 backward by
+  recomputing P from the forward's row statistics; §08 the q/k/v layout
+  [batch, heads, sequence, head_dim].
+* [NEWS] "FlashAttention技术原理详解：通过内存优化加速注意力计算"
+  (news.pikppo.com): MHA / MQA / GQA support.
+
+Modules
+-------
+``reference``  the definition, written out: S and P materialised, textbook
+               softmax, textbook chain rule for the gradients (the oracle
+               proper, used for every parity check).
+``online``     the blockwise online-softmax recurrence of [KB] §04, used only
+               to pin the oracle to the pages' worked example and to show that
+               any block size reaches the same result.
+``brute``      scalar pure-Python loops for tiny inputs (a second, independent
+               spelling of the definition).
+
+Readings of the pages where they are silent are listed in ``reference``.
+Parity status: every function here is pinned by a CPU test in
+``tests/test_oracle.py``; the only unpinned convention is the output of a
+query row that sees no key at all (O = 0, LSE = -inf), which the pages leave
+open ([KB] §04 says only that such rows must be handled).
+"""
+
+from .reference import (  # noqa: F401
+    attention_forward,
+    attention_backward,
+    head_forward,
+    head_backward,
+    visible_mask,
+)
+from .online import online_row, online_forward  # noqa: F401
+from .brute import brute_forward  # noqa: F401

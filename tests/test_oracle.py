@@ -1,0 +1,302 @@
+"""CPU pins for the float64 oracle (no GPU).
+
+Each test ties the oracle to something other than itself: the values printed
+in the worked example of page "FlashAttention：为什么少搬数据，反而算得更快" §04,
+closed forms, invariants, an independent brute-force spelling, and central
+finite differences for the gradients.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import reference as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def hand_example_inputs():
+    g = json.load(open(GOLDEN))
+    e = np.array(g["exp_scores"], dtype=np.float64)
+    # One query q = [1] and keys k_j = ln(e_j) give scores s_j = ln(e_j) at scale 1.
+    q = np.array([[1.0]])
+    k = np.log(e)[:, None]
+    v = np.array(g["values"], dtype=np.float64)[:, None]
+    return g, q, k, v
+
+
+# ---------------------------------------------------------------- forward pins
+
+def test_hand_example_one_block():
+    g, q, k, v = hand_example_inputs()
+    o, lse = oracle.head_forward(q, k, v, causal=False, scale=1.0)
+    assert o[0, 0] == pytest.approx(g["output"], abs=1e-12)
+    assert lse[0] == pytest.approx(math.log(10.0), abs=1e-12)
+    # With one-hot values the output row is the weight row itself.
+    o_w, _ = oracle.head_forward(q, k, np.eye(4), causal=False, scale=1.0)
+    np.testing.assert_allclose(o_w[0], g["full_weights"], atol=1e-12)
+
+
+def test_hand_example_two_blocks_state_by_state():
+    g, q, k, v = hand_example_inputs()
+    o, lse, trace = oracle.online_row(np.log(g["exp_scores"]), g["values"], block=g["block"])
+    assert o == pytest.approx(g["output"], abs=1e-12)
+    assert lse == pytest.approx(math.log(10.0), abs=1e-12)
+    b1, b2 = g["blocks"]
+    assert math.exp(trace[0]["m"]) == pytest.approx(b1["m_exp"], abs=1e-12)
+    assert trace[0]["l"] == pytest.approx(b1["l"], abs=1e-12)
+    assert trace[0]["U"] == pytest.approx(b1["U"], abs=1e-12)
+    assert trace[1]["a"] == pytest.approx(b2["rescale"], abs=1e-12)
+    assert trace[1]["l_rescaled"] == pytest.approx(b2["l_rescaled"], abs=1e-12)
+    assert trace[1]["U_rescaled"] == pytest.approx(b2["U_rescaled"], abs=1e-12)
+    assert math.exp(trace[1]["m"]) == pytest.approx(b2["m_exp"], abs=1e-12)
+    assert trace[1]["l"] == pytest.approx(b2["l"], abs=1e-12)
+    assert trace[1]["U"] == pytest.approx(b2["U"], abs=1e-12)
+    assert trace[1]["U"] / trace[1]["l"] == pytest.approx(g["final"]["O"], abs=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nkv", [(9, 9), (5, 13), (13, 5), (1, 11)])
+def test_rows_sum_to_one(causal, nq, nkv):
+    q = rnd((nq, 4), 1)
+    k = rnd((nkv, 4), 2)
+    p, lse = oracle.head_forward(q, k, np.eye(nkv), causal, scale=0.7)
+    vis = oracle.visible_mask(np.arange(nq), nq, nkv, causal)
+    has = vis.any(axis=1)
+    np.testing.assert_allclose(p[has].sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(p >= 0)
+    assert np.all(p[~vis] == 0)
+    # Rows that see nothing: convention O = 0, LSE = -inf.
+    assert np.all(p[~has] == 0) and np.all(np.isneginf(lse[~has]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 2, 3, 7, 64, 37])
+def test_online_equals_full(causal, block):
+    q, k, v = rnd((2, 4, 37, 8), 3), rnd((2, 2, 37, 8), 4), rnd((2, 2, 37, 8), 5)
+    o, lse = oracle.attention_forward(q, k, v, causal, 0.3)
+    o2, lse2 = oracle.online_forward(q, k, v, causal, 0.3, block)
+    np.testing.assert_allclose(o2, o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12, rtol=0)
+
+
+@settings(max_examples=40, deadline=None)
+@given(nq=st.integers(1, 9), nkv=st.integers(1, 9), d=st.integers(1, 5),
+       block=st.integers(1, 10), causal=st.booleans(), seed=st.integers(0, 10_000))
+def test_online_equals_full_property(nq, nkv, d, block, causal, seed):
+    q, k, v = rnd((1, 1, nq, d), seed), rnd((1, 1, nkv, d), seed + 1), rnd((1, 1, nkv, d), seed + 2)
+    o, lse = oracle.attention_forward(q, k, v, causal, 1.3)
+    o2, lse2 = oracle.online_forward(q, k, v, causal, 1.3, block)
+    np.testing.assert_allclose(o2, o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 5, 5, 3), (2, 4, 2, 3, 6, 4), (1, 3, 1, 6, 4, 2), (1, 2, 1, 1, 7, 3)])
+def test_brute_force_matches(causal, shape):
+    B, Hq, Hkv, nq, nkv, d = shape
+    q, k, v = rnd((B, Hq, nq, d), 6), rnd((B, Hkv, nkv, d), 7), rnd((B, Hkv, nkv, d), 8)
+    o, lse = oracle.attention_forward(q, k, v, causal, 0.45)
+    ob, lb = oracle.brute_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.45)
+    np.testing.assert_allclose(np.array(ob), o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(np.array(lb), lse, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_convexity(causal):
+    q, k, v = rnd((11, 6), 9), rnd((11, 6), 10), rnd((11, 6), 11)
+    o, _ = oracle.head_forward(q, k, v, causal, 1.0)
+    for i in range(11):
+        vis = v[: i + 1] if causal else v
+        assert np.all(o[i] >= vis.min(axis=0) - 1e-12)
+        assert np.all(o[i] <= vis.max(axis=0) + 1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nkv", [(8, 8), (3, 8), (8, 3)])
+def test_uniform_attention_closed_form(causal, nq, nkv):
+    # q = 0: every visible key has score 0, so O is the mean of the visible
+    # value rows and LSE = ln(number visible).
+    v = rnd((nkv, 5), 12)
+    o, lse = oracle.head_forward(np.zeros((nq, 5)), rnd((nkv, 5), 13), v, causal, 0.9)
+    for i in range(nq):
+        last = min(nkv - 1, i + nkv - nq) if causal else nkv - 1
+        if last < 0:
+            assert np.all(o[i] == 0) and lse[i] == -np.inf
+            continue
+        np.testing.assert_allclose(o[i], v[: last + 1].mean(axis=0), atol=1e-12)
+        assert lse[i] == pytest.approx(math.log(last + 1), abs=1e-12)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.125, 2.5])
+def test_single_key_closed_form(scale):
+    q, k, v = rnd((6, 4), 14), rnd((1, 4), 15), rnd((1, 4), 16)
+    o, lse = oracle.head_forward(q, k, v, False, scale)
+    np.testing.assert_allclose(o, np.repeat(v, 6, axis=0), atol=1e-12)
+    np.testing.assert_allclose(lse, scale * (q @ k[0]), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(causal):
+    q, k, v = rnd((7, 4), 17), rnd((9, 4), 18), rnd((9, 4), 19)
+    c = rnd(4, 20)
+    o, lse = oracle.head_forward(q, k, v, causal, 0.6)
+    o2, lse2 = oracle.head_forward(q, k + c[None, :], v, causal, 0.6)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + 0.6 * (q @ c), atol=1e-12)
+
+
+def test_permutation_invariance():
+    q, k, v = rnd((5, 4), 21), rnd((12, 4), 22), rnd((12, 4), 23)
+    perm = np.random.default_rng(24).permutation(12)
+    o, lse = oracle.head_forward(q, k, v, False, 0.8)
+    o2, lse2 = oracle.head_forward(q, k[perm], v[perm], False, 0.8)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("nq,nkv", [(6, 6), (4, 9)])
+def test_causal_row_is_prefix_attention(nq, nkv):
+    q, k, v = rnd((nq, 3), 25), rnd((nkv, 3), 26), rnd((nkv, 3), 27)
+    o, lse = oracle.head_forward(q, k, v, True, 1.1)
+    for i in range(nq):
+        last = i + nkv - nq
+        oi, li = oracle.head_forward(q[i:i + 1], k[: last + 1], v[: last + 1], False, 1.1)
+        np.testing.assert_allclose(o[i], oi[0], atol=1e-12)
+        assert lse[i] == pytest.approx(li[0], abs=1e-12)
+    if nq == nkv:
+        np.testing.assert_allclose(o[0], v[0], atol=1e-12)
+
+
+def test_sampled_rows_match_full():
+    q, k, v = rnd((20, 4), 28), rnd((20, 4), 29), rnd((20, 4), 30)
+    o, lse = oracle.head_forward(q, k, v, True, 0.5)
+    rows = np.array([0, 7, 19])
+    o2, lse2 = oracle.head_forward(q[rows], k, v, True, 0.5, row_index=rows, nq=20)
+    np.testing.assert_allclose(o2, o[rows], atol=0)
+    np.testing.assert_allclose(lse2, lse[rows], atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_mha(causal):
+    q, k, v, do = rnd((2, 6, 5, 3), 31), rnd((2, 2, 7, 3), 32), rnd((2, 2, 7, 3), 33), rnd((2, 6, 5, 3), 34)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    o, lse = oracle.attention_forward(q, k, v, causal, 0.5)
+    o2, lse2 = oracle.attention_forward(q, kr, vr, causal, 0.5)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, atol=1e-13)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal, 0.5)
+    dq2, dk2, dv2 = oracle.attention_backward(q, kr, vr, do, causal, 0.5)
+    np.testing.assert_allclose(dq, dq2, atol=1e-12)
+    np.testing.assert_allclose(dk, dk2.reshape(2, 2, 3, 7, 3).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dv, dv2.reshape(2, 2, 3, 7, 3).sum(axis=2), atol=1e-12)
+
+
+# --------------------------------------------------------------- backward pins
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = oracle.attention_forward(q, k, v, causal, scale)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_by_finite_differences(causal):
+    B, Hq, Hkv, nq, nkv, d = 1, 2, 1, 5, 7, 3
+    q, k, v, do = rnd((B, Hq, nq, d), 35), rnd((B, Hkv, nkv, d), 36), rnd((B, Hkv, nkv, d), 37), rnd((B, Hq, nq, d), 38)
+    scale = 0.8
+    grads = oracle.attention_backward(q, k, v, do, causal, scale)
+    h = 1e-6
+    for which, g in zip(range(3), grads):
+        fd = np.zeros_like(g)
+        base = [q, k, v]
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = (_loss(*plus, do, causal, scale) - _loss(*minus, do, causal, scale)) / (2 * h)
+        rel = np.linalg.norm(g - fd) / np.linalg.norm(fd)
+        assert rel <= 1e-6, (which, rel)
+
+
+def test_backward_hand_example_closed_form():
+    # dO = 1 on the worked example: dV = P, dP_j = V_j, sum_k P_k dP_k = O = 29,
+    # dS = P (V - 29) = [-1.9, -1.8, 0.4, 3.3]; dq = sum_j dS_j k_j; dk_j = dS_j q.
+    g, q, k, v = hand_example_inputs()
+    dq, dk, dv = oracle.head_backward(q, k, v, np.ones((1, 1)), causal=False, scale=1.0)
+    np.testing.assert_allclose(dv[:, 0], g["full_weights"], atol=1e-12)
+    ds = np.array([-1.9, -1.8, 0.4, 3.3])
+    np.testing.assert_allclose(dk[:, 0], ds, atol=1e-12)
+    expect_dq = float(np.sum(ds * np.log(g["exp_scores"])))
+    assert dq[0, 0] == pytest.approx(expect_dq, abs=1e-12)
+    assert dq[0, 0] == pytest.approx(2.93227337, abs=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    q, k, v, do = rnd((1, 4, 9, 5), 39), rnd((1, 2, 9, 5), 40), rnd((1, 2, 9, 5), 41), rnd((1, 4, 9, 5), 42)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal, 0.7)
+    # Each softmax row's dS sums to zero, so the key gradients sum to zero.
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # Each P row sums to one, so summing dV over keys gives the sum of dO over
+    # the queries (and heads) that read this kv head.
+    np.testing.assert_allclose(dv.sum(axis=2), do.reshape(1, 2, 2, 9, 5).sum(axis=(2, 3)), atol=1e-12)
+
+
+def test_backward_scale_dependence():
+    # dQ and dK carry one factor of scale from S = scale * QK^T; with K = 0
+    # all scores vanish, P is uniform, and dQ = scale * dS K = 0 exactly.
+    q, v, do = rnd((4, 3), 43), rnd((6, 3), 44), rnd((4, 3), 45)
+    dq, dk, dv = oracle.head_backward(q, np.zeros((6, 3)), v, do, False, 0.3)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dv, np.repeat(do.sum(axis=0, keepdims=True) / 6, 6, axis=0), atol=1e-12)
+
+
+# ------------------------------------------------- planted mistakes are caught
+
+def _catches(monkeypatch, patch_name, patched, tests):
+    monkeypatch.setattr(ref, patch_name, patched)
+    failures = 0
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            failures += 1
+    return failures
+
+
+def test_planted_causal_off_by_one_is_caught(monkeypatch):
+    orig = ref.visible_mask
+
+    def wrong(row_index, nq, nkv, causal):
+        m = orig(row_index, nq, nkv, causal)
+        if causal:
+            rows = np.asarray(row_index)[:, None]
+            m = np.arange(nkv)[None, :] < rows + (nkv - nq)
+        return m
+
+    n = _catches(monkeypatch, "visible_mask", wrong,
+                 [lambda: test_uniform_attention_closed_form(True, 8, 8),
+                  lambda: test_causal_row_is_prefix_attention(6, 6)])
+    assert n >= 1
+
+
+def test_planted_softmax_without_max_is_harmless_but_wrong_sum_is_caught(monkeypatch):
+    def wrong(s):
+        e = np.exp(s)
+        return e / (np.sum(e, axis=1, keepdims=True) + 1.0), np.log(np.sum(e, axis=1))
+
+    n = _catches(monkeypatch, "_softmax_rows", wrong,
+                 [test_hand_example_one_block, lambda: test_rows_sum_to_one(False, 9, 9)])
+    assert n >= 1
