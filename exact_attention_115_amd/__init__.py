@@ -1,0 +1,27 @@
+"""MI355X (gfx950) exact attention: FlashAttention-style forward, backward and
+split-KV decode in hand-written HIP kernels behind a C ABI (include/fa.h).
+
+Python names mirror the C entry points (``fa_fwd``, ``fa_bwd``,
+``fa_bwd_stage``, ``fa_fwd_workspace_size``, ``fa_bwd_workspace_size``,
+``fa_strerror``, ``fa_version``); ``forward`` and ``backward`` allocate the
+outputs and the workspace and raise on error.
+"""
+
+from ._lib import (  # noqa: F401
+    FA_BF16,
+    FA_F16,
+    FA_F32,
+    FA_OK,
+    FAError,
+    LIB_PATH,
+    backward,
+    fa_bwd,
+    fa_bwd_stage,
+    fa_bwd_workspace_size,
+    fa_fwd,
+    fa_fwd_workspace_size,
+    fa_strerror,
+    fa_version,
+    forward,
+    load,
+)

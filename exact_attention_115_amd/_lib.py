@@ -1,0 +1,192 @@
+"""ctypes binding of libfa.so (argument marshalling only).
+
+Each C entry point of include/fa.h has a Python function of the same name
+that takes torch tensors, checks device / dtype / contiguity / shape, and
+passes raw device pointers, sizes and the current HIP stream through. Every
+step of the computation runs in the library's kernels; PyTorch provides only
+device memory and the stream. If the library is missing this module raises:
+there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
+    -4: "FA_ERR_ALIGNMENT", -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_SCALE", -7: "FA_ERR_HIP",
+    -8: "FA_ERR_OVERLAP",
+}
+_DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_strerror(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with exact_attention_115_amd.build.build() "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    shape = [i, i, i, i, i, i]
+    lib.fa_fwd_workspace_size.argtypes = shape + [i]
+    lib.fa_fwd_workspace_size.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = shape + [i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz] + shape + [f, i, i, vp]
+    lib.fa_fwd.restype = i
+    bwd = [vp] * 9 + [vp, sz] + shape + [f, i, i, vp]
+    lib.fa_bwd.argtypes = bwd
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_stage.argtypes = [i] + bwd
+    lib.fa_bwd_stage.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(int(status)).decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, heads, sequence, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nkv, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} vs k {tuple(k.shape)}")
+    return B, Hq, Hkv, Nq, Nkv, d
+
+
+def _check(ts, dtype=None):
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def fa_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(load().fa_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, code))
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(load().fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, code))
+
+
+def fa_fwd(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None) -> int:
+    """Call fa_fwd on tensors; returns the status code (no exception)."""
+    _check({"q": q, "k": k, "v": v, "o": o}, q.dtype)
+    _check({"lse": lse}, torch.float32)
+    _check({"workspace": workspace})
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+                         B, Hq, Hkv, Nq, Nkv, d, float(scale), int(bool(causal)), _dtype_code(q),
+                         _stream(stream))
+
+
+def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream):
+    _check({"q": q, "k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv}, q.dtype)
+    _check({"lse": lse}, torch.float32)
+    _check({"workspace": workspace})
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(workspace), ws_bytes, B, Hq, Hkv, Nq, Nkv, d, float(scale), int(bool(causal)),
+            _dtype_code(q), _stream(stream))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale: float, causal: bool, stream=None) -> int:
+    """Call fa_bwd on tensors; returns the status code (no exception)."""
+    return load().fa_bwd(*_bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream))
+
+
+def fa_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, workspace, scale: float, causal: bool,
+                 stream=None) -> int:
+    """Call fa_bwd_stage on tensors; returns the status code (no exception)."""
+    return load().fa_bwd_stage(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace,
+                                                      scale, causal, stream))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """O, LSE = attention(q, k, v). Allocates o, lse and the workspace."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ws = _workspace(fa_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, q.dtype), q.device)
+    st = fa_fwd(q, k, v, o, lse, ws, _default_scale(d, scale), causal, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):
+    """dq, dk, dv of sum(do * O). Allocates the gradients and the workspace."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, q.dtype), q.device)
+    st = fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, _default_scale(d, scale), causal, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

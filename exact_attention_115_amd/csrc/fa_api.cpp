@@ -1,0 +1,287 @@
+// C-ABI entry points of libfa.so: argument checks (pure host code, run before
+// any HIP call), workspace sizing and kernel selection. See include/fa.h for
+// the contract of each call.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+size_t elem_bytes(fa_dtype dt) { return dt == FA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == FA_F32 || dt == FA_F16 || dt == FA_BF16; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + bytes};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Shape checks shared by every entry point. Returns FA_OK, or an error, and
+// sets *empty when there is nothing to compute.
+int check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int dt, bool* empty) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nkv < 0 || d < 0) return FA_ERR_SHAPE;
+  if (!valid_dtype(dt)) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hkv == 0) {
+    if (Hq != 0) return FA_ERR_SHAPE;
+  } else if (Hq % Hkv != 0) {
+    return FA_ERR_SHAPE;
+  }
+  // Element counts must fit the kernels' 64-bit offsets and 32-bit grids.
+  const long long big = 1LL << 31;
+  if ((long long)B * Hq * (((long long)Nq + 127) / 128) >= big) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * Hq * Nq >= big || (long long)B * Hkv * Nkv >= big) return FA_ERR_UNSUPPORTED;
+  *empty = (B == 0 || Hq == 0 || Nq == 0);
+  return FA_OK;
+}
+
+Problem make_problem(int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int causal,
+                     fa_dtype dt) {
+  Problem p;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nkv = Nkv; p.d = d;
+  p.G = Hkv > 0 ? Hq / Hkv : 1;
+  p.scale = scale; p.causal = causal; p.dt = dt;
+  return p;
+}
+
+int check_scale(float scale, int causal) {
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+bool is_decode(const Problem& p) { return p.Nq == 1 && p.dt != FA_F32; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+              size_t ws_bytes, int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,
+              int causal, int dt, bool* empty, Problem* prob) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nkv, d, dt, empty);
+  if (st != FA_OK) return st;
+  st = check_scale(scale, causal);
+  if (st != FA_OK) return st;
+  if (*empty) return FA_OK;
+  *prob = make_problem(B, Hq, Hkv, Nq, Nkv, d, scale, causal, (fa_dtype)dt);
+  const size_t e = elem_bytes((fa_dtype)dt);
+  const size_t qb = (size_t)B * Hq * Nq * d * e;
+  const size_t kb = (size_t)B * Hkv * Nkv * d * e;
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  if (!q || !o || !lse) return FA_ERR_NULLPTR;
+  if (kb > 0 && (!k || !v)) return FA_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 16)) return FA_ERR_ALIGNMENT;
+  if (kb > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FA_ERR_ALIGNMENT;
+  const size_t need = is_decode(*prob) ? decode_workspace_bytes(*prob) : 0;
+  if (need > 0) {
+    if (!ws) return FA_ERR_NULLPTR;
+    if (!aligned(ws, 256)) return FA_ERR_ALIGNMENT;
+    if (ws_bytes < need) return FA_ERR_WORKSPACE;
+  }
+  const Range in[3] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+  const Range out[3] = {range_of(o, qb), range_of(lse, lb), range_of(ws, need)};
+  for (const Range& a : out) {
+    for (const Range& b : in)
+      if (overlap(a, b)) return FA_ERR_OVERLAP;
+  }
+  if (overlap(out[0], out[1]) || overlap(out[0], out[2]) || overlap(out[1], out[2]))
+    return FA_ERR_OVERLAP;
+  return FA_OK;
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B,
+              int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int causal, int dt,
+              bool* empty, Problem* prob) {
+  int st = check_shape(B, Hq, Hkv, Nq, Nkv, d, dt, empty);
+  if (st != FA_OK) return st;
+  if (dt == FA_F32) return FA_ERR_UNSUPPORTED;
+  st = check_scale(scale, causal);
+  if (st != FA_OK) return st;
+  *prob = make_problem(B, Hq, Hkv, Nq, Nkv, d, scale, causal, (fa_dtype)dt);
+  const size_t e = elem_bytes((fa_dtype)dt);
+  const size_t qb = (size_t)B * Hq * Nq * d * e;
+  const size_t kb = (size_t)B * Hkv * Nkv * d * e;
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  // dk, dv must still be cleared when there are no queries, so an empty query
+  // side is not "empty" for the backward unless the key side is empty too.
+  if (kb == 0 && qb == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  *empty = false;
+  if (qb > 0 && (!q || !o || !lse || !dO || !dq)) return FA_ERR_NULLPTR;
+  if (kb > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULLPTR;
+  const void* al[9] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : al)
+    if (p && !aligned(p, 16)) return FA_ERR_ALIGNMENT;
+  const size_t need = bwd_workspace_bytes(*prob);
+  if (need > 0) {
+    if (!ws) return FA_ERR_NULLPTR;
+    if (!aligned(ws, 256)) return FA_ERR_ALIGNMENT;
+    if (ws_bytes < need) return FA_ERR_WORKSPACE;
+  }
+  const Range in[6] = {range_of(q, qb), range_of(k, kb), range_of(v, kb),
+                       range_of(o, qb), range_of(lse, lb), range_of(dO, qb)};
+  const Range out[4] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb),
+                        range_of(ws, need)};
+  for (const Range& a : out)
+    for (const Range& b : in)
+      if (overlap(a, b)) return FA_ERR_OVERLAP;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out[j])) return FA_ERR_OVERLAP;
+  return FA_OK;
+}
+
+BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws) {
+  BwdPtrs t;
+  t.q = q; t.k = k; t.v = v; t.o = o; t.lse = lse; t.dO = dO;
+  t.dq = dq; t.dk = dk; t.dv = dv;
+  const size_t acc = align_up((size_t)p.B * p.Hq * p.Nq * p.d * sizeof(float), 256);
+  t.dq_acc = static_cast<float*>(ws);
+  t.delta = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + acc) : nullptr;
+  return t;
+}
+
+int run_bwd_stage(int stage, const Problem& p, const BwdPtrs& t, hipStream_t stream) {
+  switch (stage) {
+    case 0: return to_status(launch_bwd_pre(p, t, stream));
+    case 1: return to_status(launch_bwd_main(p, t, stream));
+    case 2: return to_status(launch_bwd_dq(p, t, stream));
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+DecodeSplit decode_split(const Problem& p) {
+  // Aim for about 1024 workgroups in flight over the key range, with at least
+  // 256 keys per split so each split streams a useful run of K/V.
+  const long long units = (long long)p.B * p.Hkv;
+  const int tiles = (p.Nkv + 63) / 64;
+  long long want = (1024 + units - 1) / units;
+  long long max_splits = (p.Nkv + 255) / 256;
+  if (max_splits < 1) max_splits = 1;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  int tiles_per_split = (int)((tiles + want - 1) / want);
+  if (tiles_per_split < 1) tiles_per_split = 1;
+  DecodeSplit s;
+  s.keys_per_split = tiles_per_split * 64;
+  s.splits = p.Nkv > 0 ? (p.Nkv + s.keys_per_split - 1) / s.keys_per_split : 1;
+  return s;
+}
+
+size_t decode_workspace_bytes(const Problem& p) {
+  const DecodeSplit s = decode_split(p);
+  const size_t rows = (size_t)p.B * p.Hq * s.splits;
+  return align_up(rows * p.d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+}
+
+size_t bwd_workspace_bytes(const Problem& p) {
+  const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+  if (rows == 0) return 0;
+  return align_up(rows * p.d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" {
+
+size_t fa_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt) {
+  bool empty = false;
+  if (check_shape(B, Hq, Hkv, Nq, Nkv, d, dt, &empty) != FA_OK || empty) return 0;
+  Problem p = make_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, 0, dt);
+  return is_decode(p) ? decode_workspace_bytes(p) : 0;
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt) {
+  bool empty = false;
+  if (check_shape(B, Hq, Hkv, Nq, Nkv, d, dt, &empty) != FA_OK || empty) return 0;
+  if (dt == FA_F32) return 0;
+  Problem p = make_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, 0, dt);
+  return bwd_workspace_bytes(p);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+           size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,
+           int causal, fa_dtype dt, hipStream_t stream) {
+  bool empty = false;
+  Problem p;
+  int st = check_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nkv, d, scale,
+                     causal, dt, &empty, &p);
+  if (st != FA_OK || empty) return st;
+  FwdPtrs t{q, k, v, o, lse, workspace};
+  if (dt == FA_F32) return to_status(launch_fwd_f32(p, t, stream));
+  if (is_decode(p)) return to_status(launch_decode(p, t, stream));
+  return to_status(launch_fwd_mfma(p, t, stream));
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dO, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                 float scale, int causal, fa_dtype dt, hipStream_t stream) {
+  if (stage < 0 || stage > 2) return FA_ERR_UNSUPPORTED;
+  bool empty = false;
+  Problem p;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq,
+                     Nkv, d, scale, causal, dt, &empty, &p);
+  if (st != FA_OK || empty) return st;
+  return run_bwd_stage(stage, p, bwd_ptrs(p, q, k, v, o, lse, dO, dq, dk, dv, workspace), stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int causal, fa_dtype dt,
+           hipStream_t stream) {
+  bool empty = false;
+  Problem p;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq,
+                     Nkv, d, scale, causal, dt, &empty, &p);
+  if (st != FA_OK || empty) return st;
+  const BwdPtrs t = bwd_ptrs(p, q, k, v, o, lse, dO, dq, dk, dv, workspace);
+  for (int stage = 0; stage < 3; ++stage) {
+    st = run_bwd_stage(stage, p, t, stream);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULLPTR: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (negative size, Hkv == 0 or Hq not a multiple of Hkv)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, pass or stage";
+    case FA_ERR_ALIGNMENT: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the size the library asks for";
+    case FA_ERR_SCALE: return "scale must be finite and > 0, causal must be 0 or 1";
+    case FA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
+    case FA_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

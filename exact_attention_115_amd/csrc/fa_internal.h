@@ -1,0 +1,63 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+// Problem description after validation (all sizes positive, d in {64, 128}).
+struct Problem {
+  int B, Hq, Hkv, Nq, Nkv, d;
+  int G;             // Hq / Hkv
+  float scale;       // > 0
+  int causal;        // 0 / 1
+  fa_dtype dt;
+};
+
+struct FwdPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* ws;          // decode split state, else unused
+};
+
+struct BwdPtrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;     // [B, Hq, Nq, d] float32, in the workspace
+  float* delta;      // [B, Hq, Nq]    float32, in the workspace
+};
+
+// Decode (N_q == 1) split-KV geometry, shared by the workspace size and the
+// launcher so both always agree.
+struct DecodeSplit {
+  int splits;        // key-range splits per (b, kv head)
+  int keys_per_split;
+};
+DecodeSplit decode_split(const Problem& p);
+size_t decode_workspace_bytes(const Problem& p);
+size_t bwd_workspace_bytes(const Problem& p);
+
+// Launchers: each enqueues its kernel(s) on `stream` and returns the
+// hipError_t of the launch.
+hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+hipError_t launch_bwd_dq(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,132 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library libfa.so.
+ *
+ * The library computes exact scaled-dot-product attention the FlashAttention
+ * way: the query rows are cut into tiles, key/value tiles are streamed through
+ * on-chip memory, and every score tile is folded at once into per-row
+ * online-softmax state, so that no N_q x N_kv score or probability matrix is
+ * ever written to device memory.
+ *
+ * Pages cited (title, section):
+ *   [BLOG] "AI infra. 一层全看懂(五)Flash Attention:AI编译优化的集大成者"
+ *   [KB]   "FlashAttention：为什么少搬数据，反而算得更快"
+ *   [NEWS] "FlashAttention技术原理详解：通过内存优化加速注意力计算"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout ([KB] §08, the q/k/v layout [batch, heads, sequence, head_dim]):
+ *   q, o, dO, dq : [B, Hq,  N_q,  d]   contiguous, row-major, d fastest
+ *   k, v, dk, dv : [B, Hkv, N_kv, d]   contiguous, row-major, d fastest
+ *   lse          : [B, Hq,  N_q]       float32, always
+ * Heads ([NEWS]: MHA / MQA / GQA): Hq must be a multiple of Hkv; query head h
+ *   reads key/value head h / (Hq / Hkv). Hkv == Hq is MHA, Hkv == 1 is MQA.
+ * Scale: S = scale * Q K^T; scale must be finite and > 0 (1/sqrt(d) is usual).
+ * Causal ([KB] §02: the mask is part of the real computation): query row i
+ *   sees key j iff j <= i + (N_kv - N_q) (aligned to the bottom-right corner;
+ *   for N_q == N_kv that is j <= i, for N_q == 1 every key is visible).
+ *   A row that sees no key gets O = 0, LSE = -inf and passes no gradient.
+ * LSE ([KB] §05, the row statistic the backward rebuilds P from): natural-log
+ *   log-sum-exp of the scaled, masked score row, m + ln(l) in the notation
+ *   of [KB] §04.
+ * dtypes: FA_F32 (forward only), FA_F16, FA_BF16. Outputs have the input
+ *   dtype; all accumulation is float32; float32 -> 16-bit conversions round
+ *   to nearest even.
+ * Head dim d: 64 or 128.
+ * Pointers: device pointers, 16-byte aligned; the workspace 256-byte aligned.
+ *   Outputs must not overlap inputs. Every output element is overwritten.
+ * Ownership: the caller allocates and frees every buffer, including the
+ *   workspace (size from fa_*_workspace_size). The library allocates nothing,
+ *   frees nothing and keeps no pointer after a call returns.
+ * Execution: every call only enqueues work on `stream` (NULL = the default
+ *   stream) and returns; order consumers by stream. Calls are re-entrant; the
+ *   library has no global mutable state.
+ * Errors: arguments are checked on the host before any HIP call; on error the
+ *   call returns a negative FA_ERR_* code, enqueues nothing and leaves every
+ *   output untouched. A failed kernel launch returns FA_ERR_HIP. Empty problems
+ *   (B, Hq or N_q equal to 0) return FA_OK and enqueue nothing.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = -1,     /* a required pointer is NULL                     */
+  FA_ERR_SHAPE = -2,       /* negative size, Hkv == 0 or Hq % Hkv != 0       */
+  FA_ERR_UNSUPPORTED = -3, /* d, dtype or pass not supported                 */
+  FA_ERR_ALIGNMENT = -4,   /* pointer not 16-byte (workspace: 256) aligned   */
+  FA_ERR_WORKSPACE = -5,   /* workspace smaller than fa_*_workspace_size()   */
+  FA_ERR_SCALE = -6,       /* scale not finite or not > 0; causal not 0 / 1  */
+  FA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch    */
+  FA_ERR_OVERLAP = -8      /* an output overlaps an input                    */
+};
+
+/* Bytes of device workspace fa_fwd needs for this problem. Zero for prefill
+ * (N_q > 1) and for FA_F32; for N_q == 1 with a 16-bit dtype (decode) the
+ * key range is split across workgroups and the workspace holds each split's
+ * partial row state (O_s, LSE_s), merged with the rescaling rule of [KB] §04.
+ * Returns 0 for an invalid or empty problem. */
+size_t fa_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt);
+
+/* Bytes of device workspace fa_bwd needs: a float32 dQ accumulator
+ * [B, Hq, N_q, d] and the float32 row terms D_i = sum_c dO_ic O_ic
+ * [B, Hq, N_q]. Linear in N ([KB] §06: storage O(N), not O(N^2)).
+ * Returns 0 for an invalid or empty problem. */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt);
+
+/* Forward ([BLOG] §五, [KB] §03-§04): O = softmax(scale * Q K^T + mask) V and
+ * the row LSE. Outer loop over query tiles (one workgroup each), inner loop
+ * over the key/value tiles the tile may see, folded in with the online
+ * softmax update of [KB] §04 (m, l, U rescaled by exp(m_old - m_new)).
+ * Reads q, k, v; writes o (input dtype) and lse (float32). */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+           float scale, int causal, fa_dtype dt, hipStream_t stream);
+
+/* Backward ([KB] §05; [NEWS]): given the forward's inputs, its output o and
+ * lse, and the output gradient dO, recompute each probability tile
+ * P = exp(scale * Q K^T - LSE) and produce dq, dk, dv (input dtype):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = sum_c dO_ic O_ic,
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK, dV of a key/value head summed over the query heads that read it.
+ * FA_F16 and FA_BF16 only. Runs the three stages of fa_bwd_stage in order. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+           float scale, int causal, fa_dtype dt, hipStream_t stream);
+
+/* One stage of fa_bwd, same arguments, for callers that interleave or time
+ * the stages. Stages must run in order 0, 1, 2 on one workspace:
+ *   0  D_i = sum_c dO_ic O_ic into the workspace; clear the dQ accumulator;
+ *   1  per key/value tile: recompute P, accumulate dK, dV (written to dk, dv)
+ *      and add scale * dS K into the dQ accumulator;
+ *   2  round the dQ accumulator into dq.
+ * Any other stage value returns FA_ERR_UNSUPPORTED. */
+int fa_bwd_stage(int stage,
+                 const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                 float scale, int causal, fa_dtype dt, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
