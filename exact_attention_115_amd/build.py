@@ -38,6 +38,7 @@ COMMON = [
     f"--offload-arch={ARCH}",
     # Keep the compiler from forming packed-FP32 vector ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
     "-Wall",
     "-Wno-unused-function",
     "-I", INCLUDE,

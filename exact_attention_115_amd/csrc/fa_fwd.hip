@@ -31,13 +31,12 @@
 
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
 
 constexpr int BR = 128;     // query rows per workgroup
-constexpr int BC = 64;      // keys per tile
-constexpr int NT = 256;     // threads per workgroup
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 
@@ -51,75 +50,9 @@ struct FwdArgs {
   float scale_log2;
 };
 
-template <int D>
-struct FwdLds {
-  static constexpr int KS = D + 8;    // K tile row stride (elements), +16 B pad
-  static constexpr int VS = BC + 8;   // V^T tile row stride (elements)
-  static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * STAGE * 2;
-};
-
-// Global loads of one K/V tile held in registers between issue and LDS write.
-template <int D>
-struct TileRegs {
-  static constexpr int KCH = (BC * D / 8) / NT;      // 16-byte K chunks per thread
-  static constexpr int V_ITEMS = (BC / 4) * (D / 8);  // 4-key x 8-dim V blocks
-  u32x4 k[KCH];
-  u32x4 v[4];
-};
-
-template <int D>
-__device__ inline void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ kbase,
-                                 const uint16_t* __restrict__ vbase, int key0, int Nkv, int tid) {
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-    const int id = tid + NT * i;
-    const int key = id / (D / 8), dc = id % (D / 8);
-    r.k[i] = (key0 + key < Nkv) ? ld16(kbase + (size_t)(key0 + key) * D + dc * 8) : zero_u32x4();
-  }
-  if (tid < TileRegs<D>::V_ITEMS) {
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int key = key0 + kg * 4 + rr;
-      r.v[rr] = key < Nkv ? ld16(vbase + (size_t)key * D + dc * 8) : zero_u32x4();
-    }
-  }
-}
-
-template <int D>
-__device__ inline void store_tile(const TileRegs<D>& r, uint16_t* ks, uint16_t* vt, int tid) {
-  using L = FwdLds<D>;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::KCH; ++i) {
-    const int id = tid + NT * i;
-    const int key = id / (D / 8), dc = id % (D / 8);
-    *reinterpret_cast<u32x4*>(ks + key * L::KS + dc * 8) = r.k[i];
-  }
-  if (tid < TileRegs<D>::V_ITEMS) {
-    const int kg = tid / (D / 8), dc = tid % (D / 8);
-    // Element e of the 8 dims, for the 4 keys, packed as 4 x 16 bit.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      const uint32_t x0 = (r.v[0][w] >> sh) & 0xffffu;
-      const uint32_t x1 = (r.v[1][w] >> sh) & 0xffffu;
-      const uint32_t x2 = (r.v[2][w] >> sh) & 0xffffu;
-      const uint32_t x3 = (r.v[3][w] >> sh) & 0xffffu;
-      u32x2 out;
-      out[0] = x0 | (x1 << 16);
-      out[1] = x2 | (x3 << 16);
-      *reinterpret_cast<u32x2*>(vt + (dc * 8 + e) * L::VS + kg * 4) = out;
-    }
-  }
-}
-
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
-  using L = FwdLds<D>;
+  using L = KVTileLds<D>;
   using V8 = typename T::vec8;
   constexpr int KC = D / 16;  // k-chunks of the QK^T contraction
   constexpr int OD = D / 32;  // 32-wide output column blocks
@@ -174,17 +107,17 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
   float l_run = 0.0f;       // this half-wave's share of the running sum
 
-  TileRegs<D> regs;
+  KVTileRegs<D> regs;
   if (n_tiles > 0) {
-    load_tile<D>(regs, kbase, vbase, 0, Nkv, tid);
-    store_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
+    load_kv_tile<D>(regs, kbase, vbase, 0, Nkv, tid);
+    store_kv_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
   }
   __syncthreads();
 
   int stage = 0;
   for (int j = 0; j < n_tiles; ++j) {
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile<D>(regs, kbase, vbase, (j + 1) * BC, Nkv, tid);
+    if (more) load_kv_tile<D>(regs, kbase, vbase, (j + 1) * BC, Nkv, tid);
 
     const uint16_t* ks = smem + stage * L::STAGE;
     const uint16_t* vt = ks + L::K_ELEMS;
@@ -257,7 +190,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
 
     if (more) {
       uint16_t* nks = smem + (stage ^ 1) * L::STAGE;
-      store_tile<D>(regs, nks, nks + L::K_ELEMS, tid);
+      store_kv_tile<D>(regs, nks, nks + L::K_ELEMS, tid);
     }
     __syncthreads();
     stage ^= 1;
