@@ -1,0 +1,244 @@
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+fa_fwd (forward kernel) followed by fa_bwd's three stages (D_i and clearing
+the dQ accumulator, the key/value-stationary gradient kernel, dQ rounding),
+all through the C ABI on torch's current stream, inputs resident in HBM.
+
+Default workload: causal attention B=1, Hq=Hkv=32, N=4096, d=128, bf16
+(the pages' 4096-token, 32-head case). ``value`` is the step's algorithmic
+throughput: forward 4*B*Hq*N_q*N_kv*d FLOP, backward 2.5x that, both halved
+for causal, divided by the measured time per step.
+
+Prints ONE JSON line. ``--workload`` selects another synthetic workload for
+development measurements (decode workloads report HBM GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+METRIC = "attention fwd/bwd TFLOP/s & % bf16 MFMA peak, causal N=4096 d=128"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "bwd_main_c3_traffic.md")
+KERNEL_SOURCES = {
+    "fwd": os.path.join(ROOT, "exact_attention_115_amd", "csrc", "fa_fwd.hip"),
+    "bwd_main": os.path.join(ROOT, "exact_attention_115_amd", "csrc", "fa_bwd.hip"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on another kernel source."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    text = open(PROFILE_SUMMARY).read()
+    m_hash = re.search(r"source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes:
+        return None
+    if m_hash.group(1) != source_hash(KERNEL_SOURCES[kernel_key]):
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, budget_s):
+    """Time the float64 oracle (as it stands) on a bounded sample of whole
+    heads of the workload; returns the throughput in the bench's unit."""
+    import numpy as np
+
+    import oracle
+    from synth import make_inputs, to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v, do = make_inputs(w)
+    G = w.Hq // w.Hkv
+    per_head_flop = (w.fwd_flop() + (w.bwd_flop() if w.backward else 0.0)) / (w.B * w.Hq)
+    done = 0
+    t0 = time.perf_counter()
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in heads:
+        qh, kh, vh = to_f64(q[b, h]), to_f64(k[b, h // G]), to_f64(v[b, h // G])
+        oracle.head_forward(qh, kh, vh, w.causal, w.scale)
+        if w.backward:
+            oracle.head_backward(qh, kh, vh, to_f64(do[b, h]), w.causal, w.scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if w.Nq == 1:
+        nbytes = decode_bytes(w) * done / (w.B * w.Hq)
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{done} of {w.B * w.Hq} (batch, head) rows of {w.name}, forward, "
+                          f"float64 numpy, {dt:.1f} s"}
+    return {"value": per_head_flop * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hq} heads of {w.name} "
+                      f"({'forward + backward' if w.backward else 'forward'}), float64 numpy, "
+                      f"{dt:.1f} s; algorithmic FLOP counted as on the GPU"}
+
+
+def decode_bytes(w):
+    e = 2 if w.dtype != "f32" else 4
+    return (w.B * w.Hq * w.Nq * w.d * e * 2 + 2 * w.B * w.Hkv * w.Nkv * w.d * e
+            + 4 * w.B * w.Hq * w.Nq)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "implemented (heads would shard across GPUs with no "
+                                   "communication)", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import exact_attention_115_amd as fa
+    from synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v, do = make_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    do = do.to(dev) if do is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    fws = fa.fa_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, q.dtype)
+    fwd_ws = torch.empty(fws, dtype=torch.uint8, device=dev) if fws else None
+    bwd = w.backward
+    if bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, q.dtype)
+        bwd_ws = torch.empty(bws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    names = ["fwd"] + (["bwd_pre", "bwd_main", "bwd_dq"] if bwd else [])
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        st = fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd")
+        if events is not None:
+            events[1].record(stream)
+        if bwd:
+            for s in range(3):
+                st = fa.fa_bwd_stage(s, q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale,
+                                     w.causal, stream)
+                if st != 0:
+                    raise fa.FAError(st, f"fa_bwd_stage {s}")
+                if events is not None:
+                    events[2 + s].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    per_kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                     for j, n in enumerate(names)}
+
+    fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
+    out = {
+        "metric": METRIC if args.workload == "c3" else f"attention throughput, {w.name}",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to the storage dtype",
+        "config": {"workload": f"{'causal' if w.causal else 'non-causal'} attention "
+                               f"{'forward+backward' if bwd else 'forward'} B={w.B} Hq={w.Hq} "
+                               f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}",
+                   "name": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N_q": w.Nq,
+                   "N_kv": w.Nkv, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel_ms.items()},
+    }
+    if w.Nq == 1:
+        # Decode: HBM-bound, reported as algorithmic bytes per second.
+        nbytes = decode_bytes(w)
+        gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+        out.update({"value": round(gbs, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)})
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "kernel": "decode split + combine (one fa_fwd call)",
+                           "algorithmic_bytes": nbytes}
+    else:
+        tflops = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+        fwd_t = fwd_flop / (per_kernel_ms["fwd"] * 1e-3) / 1e12
+        out.update({"value": round(tflops, 2), "unit": "TFLOP/s",
+                    "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                    "fwd_tflops": round(fwd_t, 2),
+                    "fwd_pct_peak": round(100 * fwd_t / PEAK_BF16_TFLOPS, 2)})
+        if bwd:
+            bwd_ms = per_kernel_ms["bwd_pre"] + per_kernel_ms["bwd_main"] + per_kernel_ms["bwd_dq"]
+            bwd_t = bwd_flop / (bwd_ms * 1e-3) / 1e12
+            out.update({"bwd_tflops": round(bwd_t, 2), "bwd_pct_peak": round(100 * bwd_t / PEAK_BF16_TFLOPS, 2)})
+        # Roofline of the dominant kernel (the longest average launch).
+        dom = max(per_kernel_ms, key=per_kernel_ms.get)
+        flop = {"fwd": fwd_flop, "bwd_main": bwd_flop}.get(dom)
+        if flop is not None:
+            ach = flop / (per_kernel_ms[dom] * 1e-3) / 1e12
+            out["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                               "traffic": read_traffic(dom) if args.workload == "c3" else None,
+                               "kernel": dom, "avg_launch_ms": round(per_kernel_ms[dom], 4),
+                               "algorithmic_flop_per_launch": flop}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = zero16();
-        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::KS + h * 8;
+        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RS + h * 8;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
           s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(krow + kc * 16)), qf[kc], s[kb]);
@@ -141,8 +141,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
         float pv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-        const V8 va = as_vec8<T>(
-            *reinterpret_cast<const u32x4*>(vt + (wave * 32 + c) * L::VS + ch * 16 + h * 8));
+        const V8 va = load_vt_operand<T, L::RS>(vt, h, c, ch * 16, wave * 32);
         oacc = T::mfma(va, pack8<T>(pv), oacc);
       }
     }

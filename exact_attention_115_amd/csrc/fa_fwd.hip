@@ -21,8 +21,8 @@
 //   are, unchanged, the B operand (P^T) of O^T += V^T P^T, so P never leaves
 //   registers.
 // * O^T = V^T P^T keeps the output accumulator lane = query as well, so the
-//   per-row rescale is lane-local. V^T is formed when the tile is written to
-//   LDS (4 keys x 8 dims per thread, transposed in registers).
+//   per-row rescale is lane-local. V stays row-major in LDS; its transpose is
+//   taken by the gfx950 transposed LDS read (see fa_tile.h).
 // * K and V^T tiles are double-buffered in LDS; the global loads of tile j+1
 //   are issued before the matrix-core work of tile j, one barrier per tile.
 // * Exponentials use exp2 with log2(e) folded into the scale; the LSE is
@@ -39,6 +39,8 @@ namespace {
 constexpr int BR = 128;     // query rows per workgroup
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
+// Growth of the row maximum (log2 units) tolerated before rescaling.
+constexpr float kRescaleSlack = 8.0f;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -51,7 +53,7 @@ struct FwdArgs {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   using L = KVTileLds<D>;
   using V8 = typename T::vec8;
   constexpr int KC = D / 16;  // k-chunks of the QK^T contraction
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = zero16();
-        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::KS + h * 8;
+        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RS + h * 8;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           const V8 ka = as_vec8<T>(*reinterpret_cast<const u32x4*>(krow + kc * 16));
@@ -146,16 +148,28 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r)
             if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
       }
-      // Online softmax update ([KB] §04) in log2 units.
+      // Online softmax update ([KB] §04) in log2 units. The running
+      // maximum is only moved (and U, l rescaled) when some row of the wave
+      // sees a score more than kRescaleSlack above it; otherwise the stale
+      // maximum is kept. Both U and l are always relative to the same m, so
+      // O = U / l and LSE = m + log l are unchanged; p stays <= 2^slack.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      mx = fmaxf(mx, swap_halves(mx)) * a.scale_log2;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int od = 0; od < OD; ++od)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
       float psum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -165,12 +179,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
           s[kb][r] = p;
           psum += p;
         }
-      l_run = fmaf(alpha, l_run, psum);
-      m_run = m_new;
-#pragma unroll
-      for (int od = 0; od < OD; ++od)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
+      l_run += psum;
 
       // O^T += V^T P^T over four 16-key chunks.
 #pragma unroll
@@ -181,8 +190,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(FwdArgs a) {
         const V8 pf = pack8<T>(pv);
 #pragma unroll
         for (int od = 0; od < OD; ++od) {
-          const V8 va = as_vec8<T>(
-              *reinterpret_cast<const u32x4*>(vt + (od * 32 + c) * L::VS + ch * 16 + h * 8));
+          const V8 va = load_vt_operand<T, L::RS>(vt, h, c, ch * 16, od * 32);
           oacc[od] = T::mfma(va, pf, oacc[od]);
         }
       }
