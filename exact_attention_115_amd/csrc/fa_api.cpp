@@ -155,9 +155,19 @@ BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, 
   BwdPtrs t;
   t.q = q; t.k = k; t.v = v; t.o = o; t.lse = lse; t.dO = dO;
   t.dq = dq; t.dk = dk; t.dv = dv;
-  const size_t acc = align_up((size_t)p.B * p.Hq * p.Nq * p.d * sizeof(float), 256);
-  t.dq_acc = static_cast<float*>(ws);
-  t.delta = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + acc) : nullptr;
+  const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+  const size_t acc = align_up(rows * p.d * sizeof(float), 256);
+  const size_t del = align_up(rows * sizeof(float), 256);
+  char* base = static_cast<char*>(ws);
+  t.dq_acc = reinterpret_cast<float*>(base);
+  t.delta = base ? reinterpret_cast<float*>(base + acc) : nullptr;
+  t.dk_part = t.dv_part = nullptr;
+  const int gs = bwd_group_split(p);
+  if (gs > 1 && base) {
+    const size_t part = align_up((size_t)gs * p.B * p.Hkv * p.Nkv * p.d * sizeof(float), 256);
+    t.dk_part = reinterpret_cast<float*>(base + acc + del);
+    t.dv_part = reinterpret_cast<float*>(base + acc + del + part);
+  }
   return t;
 }
 
@@ -196,10 +206,26 @@ size_t decode_workspace_bytes(const Problem& p) {
   return align_up(rows * p.d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
 }
 
+int bwd_group_split(const Problem& p) {
+  // Aim for at least ~512 workgroups; split the G query heads of a key block
+  // across workgroups (each sums its share of dK, dV) when there are fewer.
+  const long long blocks = (long long)((p.Nkv + 127) / 128) * p.B * p.Hkv;
+  if (blocks <= 0 || p.G <= 1 || blocks >= 512) return 1;
+  int want = (int)((512 + blocks - 1) / blocks);
+  int best = 1;
+  for (int s = 1; s <= p.G; ++s)
+    if (p.G % s == 0 && s <= want) best = s;
+  return best;
+}
+
 size_t bwd_workspace_bytes(const Problem& p) {
   const size_t rows = (size_t)p.B * p.Hq * p.Nq;
-  if (rows == 0) return 0;
-  return align_up(rows * p.d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+  const size_t kv = (size_t)p.B * p.Hkv * p.Nkv * p.d;
+  if (rows == 0 && kv == 0) return 0;
+  size_t bytes = align_up(rows * p.d * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+  const int gs = bwd_group_split(p);
+  if (gs > 1) bytes += 2 * align_up((size_t)gs * kv * sizeof(float), 256);
+  return bytes;
 }
 
 }  // namespace fa

@@ -13,21 +13,29 @@
 // Three stages on one stream:
 //   0  pre:   D_i for every query row; clear the float32 dQ accumulator.
 //   1  main:  one workgroup per 128-key block of one (b, kv head). K and V of
-//             the block stay in registers; the workgroup loops over the query
-//             heads of the group (GQA/MQA: dK, dV summed in registers, no
-//             atomics) and over the 64-row query tiles that can see the block
-//             (causal: only tiles at or below the diagonal). Per tile:
+//             the block stay in registers (and K row-major in LDS); the
+//             workgroup loops over the query heads of the group (GQA/MQA: dK,
+//             dV summed in registers, no atomics) and over the 64-row query
+//             tiles that can see the block (causal: only tiles at or below
+//             the diagonal). Q / dO tiles are double-buffered in LDS, the
+//             next one loading while the current one is used. Per tile:
 //               S = Q K^T and dP = dO V^T  (lane = key, 16 query rows / lane)
 //               P, dS in registers
-//               dV^T += dO^T P,  dK^T += Q^T dS   (accumulated in registers)
+//               dV^T += dO^T P,  dK^T += Q^T dS   (accumulated in registers;
+//               the transposed operands come from transposed LDS reads)
 //               dS -> LDS as [query][key]; dQ += dS K for the 128 keys,
 //               added to the float32 accumulator with atomics
-//             and finally writes dK (times scale) and dV.
-//   2  dq:    dq = scale * accumulator, rounded to the input dtype.
+//             and finally writes dK (times scale) and dV. When there are too
+//             few key blocks to fill the GPU (e.g. MQA), the query heads of a
+//             group are split over several workgroups, which write float32
+//             partial dK, dV to the workspace instead.
+//   2  dq:    dq = scale * accumulator, rounded to the input dtype; with a
+//             split head group, also dK = scale * sum of partials, dV = sum.
 #include <math.h>
 
 #include "fa_device.h"
 #include "fa_internal.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -49,7 +57,9 @@ struct BwdArgs {
   uint16_t* dv;
   float* dq_acc;
   float* delta;
-  int Hq, Hkv, G, Nq, Nkv, n_kblocks, n_bk;
+  float* dk_part;
+  float* dv_part;
+  int Hq, Hkv, G, Nq, Nkv, n_kblocks, n_bk, gsplit;
   float scale, scale_log2;
 };
 
@@ -87,31 +97,66 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------- stage 1
 template <int D>
 struct BwdLds {
-  static constexpr int QS = D + 8;     // Q, dO row stride   [BQ][D]
-  static constexpr int TS = BQ + 8;    // Q^T, dO^T stride   [D][BQ]
-  static constexpr int SS = BKV + 8;   // dS [BQ][BKV], K^T [D][BKV] stride
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = Q_OFF + BQ * QS;
-  static constexpr int QT_OFF = DO_OFF + BQ * QS;
-  static constexpr int DOT_OFF = QT_OFF + D * TS;
-  static constexpr int DS_OFF = DOT_OFF + D * TS;
-  static constexpr int KT_OFF = DS_OFF + BQ * SS;
-  static constexpr int ELEMS = KT_OFF + D * SS;
+  static constexpr int RS = D + 16;    // row stride of Q, dO, K tiles (32-byte pad)
+  static constexpr int SS = BKV + 16;  // row stride of dS [BQ][BKV]
+  static constexpr int TILE = BQ * RS;
+  static constexpr int Q_OFF = 0;                // [2][BQ][RS]
+  static constexpr int DO_OFF = Q_OFF + 2 * TILE;  // [2][BQ][RS]
+  static constexpr int DS_OFF = DO_OFF + 2 * TILE; // [BQ][SS]
+  static constexpr int K_OFF = DS_OFF + BQ * SS;   // [BKV][RS]
+  static constexpr int ELEMS = K_OFF + BKV * RS;
 };
 
-// Write a block of 4 rows x 8 columns (held as 4 x 16 bytes) to LDS both
-// row-major and transposed (8 runs of 4 elements).
-__device__ inline void put_rows_and_transpose(const u32x4 (&x)[4], uint16_t* rm, int rm_stride,
-                                              uint16_t* tr, int tr_stride) {
+// Q / dO tile of BQ rows (plus the rows' LSE and D) held in registers between
+// the global loads and the LDS write, so the loads of the next tile overlap
+// the work on the current one.
+template <int D>
+struct QTileRegs {
+  static constexpr int CH = (BQ * D / 8) / NTB;  // 16-byte chunks per thread, per tensor
+  u32x4 q[CH];
+  u32x4 g[CH];
+  float lse2, delta;
+};
+
+template <int D>
+__device__ inline void load_q_tile(QTileRegs<D>& r, const uint16_t* __restrict__ qh,
+                                   const uint16_t* __restrict__ doh, const float* __restrict__ lse,
+                                   const float* __restrict__ delta, int qi0, int Nq, int tid) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<u32x4*>(rm + rr * rm_stride) = x[rr];
+  for (int i = 0; i < QTileRegs<D>::CH; ++i) {
+    const int id = tid + NTB * i;
+    const int row = id / (D / 8), dc = id % (D / 8);
+    const bool in = qi0 + row < Nq;
+    const size_t off = (size_t)(qi0 + row) * D + dc * 8;
+    r.q[i] = in ? ld16(qh + off) : zero_u32x4();
+    r.g[i] = in ? ld16(doh + off) : zero_u32x4();
+  }
+  if (tid < BQ) {
+    const int row = qi0 + tid;
+    r.lse2 = INFINITY;  // rows past the end, and rows that saw no key: P = 0
+    r.delta = 0.0f;
+    if (row < Nq) {
+      const float l = lse[row];
+      if (l != -INFINITY) r.lse2 = l * LOG2E;
+      r.delta = delta[row];
+    }
+  }
+}
+
+template <int D>
+__device__ inline void store_q_tile(const QTileRegs<D>& r, uint16_t* qs, uint16_t* gs,
+                                    float* lse_s, float* del_s, int tid) {
+  using L = BwdLds<D>;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1, sh = (e & 1) * 16;
-    u32x2 out;
-    out[0] = ((x[0][w] >> sh) & 0xffffu) | (((x[1][w] >> sh) & 0xffffu) << 16);
-    out[1] = ((x[2][w] >> sh) & 0xffffu) | (((x[3][w] >> sh) & 0xffffu) << 16);
-    *reinterpret_cast<u32x2*>(tr + e * tr_stride) = out;
+  for (int i = 0; i < QTileRegs<D>::CH; ++i) {
+    const int id = tid + NTB * i;
+    const int row = id / (D / 8), dc = id % (D / 8);
+    *reinterpret_cast<u32x4*>(qs + row * L::RS + dc * 8) = r.q[i];
+    *reinterpret_cast<u32x4*>(gs + row * L::RS + dc * 8) = r.g[i];
+  }
+  if (tid < BQ) {
+    lse_s[tid] = r.lse2;
+    del_s[tid] = r.delta;
   }
 }
 
@@ -121,11 +166,10 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
   using V8 = typename T::vec8;
   constexpr int KC = D / 16;
   constexpr int OD = D / 32;
-  constexpr int ITEMS = (BQ / 4) * (D / 8);  // 4x8 blocks of a Q / dO tile
 
   __shared__ __attribute__((aligned(16))) uint16_t sm[L::ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse_s[BQ];
-  __shared__ __attribute__((aligned(16))) float del_s[BQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float del_s[2][BQ];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -135,14 +179,17 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
 
   // Key blocks in ascending order: under the causal mask the first blocks
   // are seen by the most query tiles, so the heaviest work starts first.
-  const int kt = blockIdx.x / a.n_bk;
-  const int bk = blockIdx.x % a.n_bk;
+  const int gsi = blockIdx.x % a.gsplit;   // which share of the head group
+  const int rest = blockIdx.x / a.gsplit;
+  const int kt = rest / a.n_bk;
+  const int bk = rest % a.n_bk;
   const int b = bk / a.Hkv;
   const int hkv = bk % a.Hkv;
   const int Nq = a.Nq, Nkv = a.Nkv;
   const int offset = Nkv - Nq;
   const int kblk0 = kt * BKV;
-  const int my_key = kblk0 + wave * 32 + c;  // the key this lane's column holds
+  const int kw0 = kblk0 + wave * 32;  // first key of this wave
+  const int my_key = kw0 + c;         // the key this lane's column holds
 
   const uint16_t* kbase = a.k + (size_t)bk * Nkv * D;
   const uint16_t* vbase = a.v + (size_t)bk * Nkv * D;
@@ -155,26 +202,13 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
     kf[kc] = as_vec8<T>(in ? ld16(kbase + (size_t)my_key * D + kc * 16 + h * 8) : zero_u32x4());
     vf[kc] = as_vec8<T>(in ? ld16(vbase + (size_t)my_key * D + kc * 16 + h * 8) : zero_u32x4());
   }
-  // K^T of the block in LDS for dQ = dS K.
-  {
-    constexpr int KITEMS = (BKV / 4) * (D / 8);
-    for (int it = tid; it < KITEMS; it += NTB) {
-      const int r4 = it / (D / 8), dc = it % (D / 8);
-      u32x4 x[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = kblk0 + r4 * 4 + rr;
-        x[rr] = key < Nkv ? ld16(kbase + (size_t)key * D + dc * 8) : zero_u32x4();
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        u32x2 out;
-        out[0] = ((x[0][w] >> sh) & 0xffffu) | (((x[1][w] >> sh) & 0xffffu) << 16);
-        out[1] = ((x[2][w] >> sh) & 0xffffu) | (((x[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(sm + L::KT_OFF + (dc * 8 + e) * L::SS + r4 * 4) = out;
-      }
-    }
+  // The key block row-major in LDS: the B operand of dQ = dS K is read from
+  // it with transposed reads.
+  for (int id = tid; id < BKV * (D / 8); id += NTB) {
+    const int key = id / (D / 8), dc = id % (D / 8);
+    const bool in = kblk0 + key < Nkv;
+    *reinterpret_cast<u32x4*>(sm + L::K_OFF + key * L::RS + dc * 8) =
+        in ? ld16(kbase + (size_t)(kblk0 + key) * D + dc * 8) : zero_u32x4();
   }
 
   f32x16 dk[OD], dv[OD];
@@ -184,153 +218,169 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
     dv[od] = zero16();
   }
 
-  // Query tiles that can see some key of this block.
+  // Query tiles that can see some key of this block, for each of this
+  // workgroup's query heads, flattened into one loop.
   const int n_qt = (Nq + BQ - 1) / BQ;
   int qt_begin = 0;
   if (CAUSAL) {
     const int first_q = kblk0 - offset;  // first query that sees key kblk0
-    qt_begin = first_q <= 0 ? 0 : first_q / BQ;
+    qt_begin = first_q <= 0 ? 0 : min(n_qt, first_q / BQ);
   }
+  const int per_head = n_qt - qt_begin;
+  const int heads = a.G / a.gsplit;
+  const int total = per_head * heads;
+  const int hq0 = hkv * a.G + gsi * heads;
 
-  for (int g = 0; g < a.G; ++g) {
-    const int hq = hkv * a.G + g;
+  QTileRegs<D> regs;
+  if (total > 0) {
+    const size_t rb = ((size_t)b * a.Hq + hq0) * Nq;
+    load_q_tile<D>(regs, a.q + rb * D, a.dO + rb * D, a.lse + rb, a.delta + rb, qt_begin * BQ, Nq, tid);
+    store_q_tile<D>(regs, sm + L::Q_OFF, sm + L::DO_OFF, lse_s[0], del_s[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    const int hq = hq0 + it / per_head;
+    const int qi0 = (qt_begin + it % per_head) * BQ;
     const size_t rowbase = ((size_t)b * a.Hq + hq) * Nq;
-    const uint16_t* qh = a.q + rowbase * D;
-    const uint16_t* doh = a.dO + rowbase * D;
-    for (int qt = qt_begin; qt < n_qt; ++qt) {
-      const int qi0 = qt * BQ;
-      // ---- stage the Q and dO tiles (row-major and transposed), LSE, D.
-      if (tid < ITEMS) {
-        const int r4 = tid / (D / 8), dc = tid % (D / 8);
-        u32x4 xq[4], xd[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = qi0 + r4 * 4 + rr;
-          const bool in = row < Nq;
-          xq[rr] = in ? ld16(qh + (size_t)row * D + dc * 8) : zero_u32x4();
-          xd[rr] = in ? ld16(doh + (size_t)row * D + dc * 8) : zero_u32x4();
-        }
-        put_rows_and_transpose(xq, sm + L::Q_OFF + (r4 * 4) * L::QS + dc * 8, L::QS,
-                               sm + L::QT_OFF + (dc * 8) * L::TS + r4 * 4, L::TS);
-        put_rows_and_transpose(xd, sm + L::DO_OFF + (r4 * 4) * L::QS + dc * 8, L::QS,
-                               sm + L::DOT_OFF + (dc * 8) * L::TS + r4 * 4, L::TS);
-      }
-      if (tid < BQ) {
-        const int row = qi0 + tid;
-        float l2 = INFINITY, dl = 0.0f;
-        if (row < Nq) {
-          const float l = a.lse[rowbase + row];
-          // A row that saw no key (LSE = -inf) has P = 0: use +inf.
-          l2 = (l == -INFINITY) ? INFINITY : l * LOG2E;
-          dl = a.delta[rowbase + row];
-        }
-        lse_s[tid] = l2;
-        del_s[tid] = dl;
-      }
-      __syncthreads();
+    const bool more = it + 1 < total;
+    if (more) {
+      const int hq_n = hq0 + (it + 1) / per_head;
+      const int qi_n = (qt_begin + (it + 1) % per_head) * BQ;
+      const size_t rb = ((size_t)b * a.Hq + hq_n) * Nq;
+      load_q_tile<D>(regs, a.q + rb * D, a.dO + rb * D, a.lse + rb, a.delta + rb, qi_n, Nq, tid);
+    }
+    const uint16_t* qs = sm + L::Q_OFF + buf * L::TILE;
+    const uint16_t* gs = sm + L::DO_OFF + buf * L::TILE;
+    const float* ls = lse_s[buf];
+    const float* ds_ = del_s[buf];
 
-      // ---- S = Q K^T and dP = dO V^T (rows: query, columns: this wave's keys)
-      f32x16 s[2], dp[2];
+    // ---- S = Q K^T and dP = dO V^T (rows: query, columns: this wave's keys)
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = zero16();
-        dp[qb] = zero16();
-        const uint16_t* qrow = sm + L::Q_OFF + (qb * 32 + row_perm(c)) * L::QS + h * 8;
-        const uint16_t* drow = sm + L::DO_OFF + (qb * 32 + row_perm(c)) * L::QS + h * 8;
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = zero16();
+      dp[qb] = zero16();
+      const uint16_t* qrow = qs + (qb * 32 + row_perm(c)) * L::RS + h * 8;
+      const uint16_t* grow = gs + (qb * 32 + row_perm(c)) * L::RS + h * 8;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          s[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(qrow + kc * 16)), kf[kc], s[qb]);
-          dp[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(drow + kc * 16)), vf[kc], dp[qb]);
-        }
-      }
-      // ---- P = exp(scale S - LSE) (masked -> 0), dS = P (dP - D)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lq = qb * 32 + acc_key(h, r);
-          const int query = qi0 + lq;
-          bool vis = my_key < Nkv && query < Nq;
-          if (CAUSAL) vis = vis && (my_key <= query + offset);
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[qb][r], a.scale_log2, -lse_s[lq])) : 0.0f;
-          s[qb][r] = p;
-          dp[qb][r] = p * (dp[qb][r] - del_s[lq]);
-        }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (contraction over the 64 queries)
-#pragma unroll
-      for (int ch = 0; ch < BQ / 16; ++ch) {
-        float pv[8], dv8[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-          dv8[t] = dp[ch >> 1][(ch & 1) * 8 + t];
-        }
-        const V8 pf = pack8<T>(pv);
-        const V8 dsf = pack8<T>(dv8);
-#pragma unroll
-        for (int od = 0; od < OD; ++od) {
-          const V8 a1 = as_vec8<T>(*reinterpret_cast<const u32x4*>(
-              sm + L::DOT_OFF + (od * 32 + c) * L::TS + ch * 16 + h * 8));
-          dv[od] = T::mfma(a1, pf, dv[od]);
-          const V8 a2 = as_vec8<T>(*reinterpret_cast<const u32x4*>(
-              sm + L::QT_OFF + (od * 32 + c) * L::TS + ch * 16 + h * 8));
-          dk[od] = T::mfma(a2, dsf, dk[od]);
-        }
-      }
-      // ---- dS to LDS as [query][key] (16-bit) for the dQ product.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sm[L::DS_OFF + (qb * 32 + acc_key(h, r)) * L::SS + wave * 32 + c] = T::from_float(dp[qb][r]);
-      __syncthreads();
-
-      // ---- dQ[query][d] += sum over the block's 128 keys of dS K.
-      // Output tiles (query block qb, dim block od); D = 128: 8 tiles, 2 per
-      // wave; D = 64: 4 tiles, 1 per wave. Lane = dim column, so each atomic
-      // instruction touches 32 consecutive floats of two rows.
-      constexpr int TILES = 2 * OD;
-      constexpr int PER_WAVE = TILES / 4;
-#pragma unroll
-      for (int ti = 0; ti < PER_WAVE; ++ti) {
-        const int tile = wave * PER_WAVE + ti;
-        const int qb = tile / OD, od = tile % OD;
-        f32x16 acc = zero16();
-        const uint16_t* dsrow = sm + L::DS_OFF + (qb * 32 + c) * L::SS + h * 8;
-        const uint16_t* ktrow = sm + L::KT_OFF + (od * 32 + c) * L::SS + h * 8;
-#pragma unroll
-        for (int ch = 0; ch < BKV / 16; ++ch) {
-          const V8 dsa = as_vec8<T>(*reinterpret_cast<const u32x4*>(dsrow + ch * 16));
-          const V8 ktb = as_vec8<T>(*reinterpret_cast<const u32x4*>(ktrow + ch * 16));
-          acc = T::mfma(dsa, ktb, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = qi0 + qb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (query < Nq)
-            atomicAdd(a.dq_acc + (rowbase + query) * D + od * 32 + c, acc[r]);
-        }
+      for (int kc = 0; kc < KC; ++kc) {
+        s[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(qrow + kc * 16)), kf[kc], s[qb]);
+        dp[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(grow + kc * 16)), vf[kc], dp[qb]);
       }
     }
+    // ---- P = exp(scale S - LSE), dS = P (dP - D); masks only where needed.
+    const bool need_mask = (kw0 + 32 > Nkv) || (CAUSAL && kw0 + 31 > qi0 + offset);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lq = qb * 32 + acc_key(h, r);
+        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], a.scale_log2, -ls[lq]));
+        if (need_mask) {
+          bool vis = my_key < Nkv;
+          if (CAUSAL) vis = vis && (my_key <= qi0 + lq + offset);
+          p = vis ? p : 0.0f;
+        }
+        s[qb][r] = p;
+        dp[qb][r] = p * (dp[qb][r] - ds_[lq]);
+      }
+    // ---- dV^T += dO^T P and dK^T += Q^T dS (contraction over the BQ queries);
+    // the transposed operands come from transposed LDS reads.
+#pragma unroll
+    for (int ch = 0; ch < BQ / 16; ++ch) {
+      float pv[8], dv8[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
+        dv8[t] = dp[ch >> 1][(ch & 1) * 8 + t];
+      }
+      const V8 pf = pack8<T>(pv);
+      const V8 dsf = pack8<T>(dv8);
+#pragma unroll
+      for (int od = 0; od < OD; ++od) {
+        dv[od] = T::mfma(load_vt_operand<T, L::RS>(gs, h, c, ch * 16, od * 32), pf, dv[od]);
+        dk[od] = T::mfma(load_vt_operand<T, L::RS>(qs, h, c, ch * 16, od * 32), dsf, dk[od]);
+      }
+    }
+    // ---- dS to LDS as [query][key] (16-bit) for the dQ product.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sm[L::DS_OFF + (qb * 32 + acc_key(h, r)) * L::SS + wave * 32 + c] = T::from_float(dp[qb][r]);
+    __syncthreads();
+
+    // ---- dQ[query][d] += sum over the block's 128 keys of dS K.
+    // Output tiles (query block qb, dim block od); D = 128: 8 tiles, 2 per
+    // wave; D = 64: 4 tiles, 1 per wave. Lane = dim column, so each atomic
+    // instruction touches 32 consecutive floats of two rows.
+    constexpr int TILES = 2 * OD;
+    constexpr int PER_WAVE = TILES / 4;
+#pragma unroll
+    for (int ti = 0; ti < PER_WAVE; ++ti) {
+      const int tile = wave * PER_WAVE + ti;
+      const int qb = tile / OD, od = tile % OD;
+      f32x16 acc = zero16();
+      const uint16_t* dsrow = sm + L::DS_OFF + (qb * 32 + c) * L::SS + h * 8;
+#pragma unroll
+      for (int ch = 0; ch < BKV / 16; ++ch) {
+        const V8 dsa = as_vec8<T>(*reinterpret_cast<const u32x4*>(dsrow + ch * 16));
+        acc = T::mfma(dsa, load_vt_operand<T, L::RS>(sm + L::K_OFF, h, c, ch * 16, od * 32), acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int query = qi0 + qb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (query < Nq) atomicAdd(a.dq_acc + (rowbase + query) * D + od * 32 + c, acc[r]);
+      }
+    }
+
+    if (more)
+      store_q_tile<D>(regs, sm + L::Q_OFF + (buf ^ 1) * L::TILE, sm + L::DO_OFF + (buf ^ 1) * L::TILE,
+                      lse_s[buf ^ 1], del_s[buf ^ 1], tid);
+    __syncthreads();
   }
 
-  // ---- write dK = scale * (sum dS^T Q), dV (lane = key, 16 dims per tile).
+  // ---- dK = scale * (sum dS^T Q) and dV (lane = key, 16 dims per tile); a
+  // split head group writes float32 partial sums that stage 2 adds up.
   if (my_key < Nkv) {
-    uint16_t* dkrow = a.dk + ((size_t)bk * Nkv + my_key) * D;
-    uint16_t* dvrow = a.dv + ((size_t)bk * Nkv + my_key) * D;
+    const size_t row = (size_t)bk * Nkv + my_key;
+    if (a.gsplit == 1) {
+      uint16_t* dkrow = a.dk + row * D;
+      uint16_t* dvrow = a.dv + row * D;
 #pragma unroll
-    for (int od = 0; od < OD; ++od)
+      for (int od = 0; od < OD; ++od)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 ok, ov;
-        ok[0] = pack2<T>(dk[od][4 * g4 + 0] * a.scale, dk[od][4 * g4 + 1] * a.scale);
-        ok[1] = pack2<T>(dk[od][4 * g4 + 2] * a.scale, dk[od][4 * g4 + 3] * a.scale);
-        ov[0] = pack2<T>(dv[od][4 * g4 + 0], dv[od][4 * g4 + 1]);
-        ov[1] = pack2<T>(dv[od][4 * g4 + 2], dv[od][4 * g4 + 3]);
-        const int d0 = od * 32 + g4 * 8 + h * 4;
-        *reinterpret_cast<u32x2*>(dkrow + d0) = ok;
-        *reinterpret_cast<u32x2*>(dvrow + d0) = ov;
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 ok, ov;
+          ok[0] = pack2<T>(dk[od][4 * g4 + 0] * a.scale, dk[od][4 * g4 + 1] * a.scale);
+          ok[1] = pack2<T>(dk[od][4 * g4 + 2] * a.scale, dk[od][4 * g4 + 3] * a.scale);
+          ov[0] = pack2<T>(dv[od][4 * g4 + 0], dv[od][4 * g4 + 1]);
+          ov[1] = pack2<T>(dv[od][4 * g4 + 2], dv[od][4 * g4 + 3]);
+          const int d0 = od * 32 + g4 * 8 + h * 4;
+          *reinterpret_cast<u32x2*>(dkrow + d0) = ok;
+          *reinterpret_cast<u32x2*>(dvrow + d0) = ov;
+        }
+    } else {
+      const size_t plane = (size_t)a.n_bk * Nkv * D;
+      float* pk = a.dk_part + gsi * plane + row * D;
+      float* pv = a.dv_part + gsi * plane + row * D;
+#pragma unroll
+      for (int od = 0; od < OD; ++od)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 xk, xv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xk[i] = dk[od][4 * g4 + i];
+            xv[i] = dv[od][4 * g4 + i];
+          }
+          const int d0 = od * 32 + g4 * 8 + h * 4;
+          *reinterpret_cast<f32x4*>(pk + d0) = xk;
+          *reinterpret_cast<f32x4*>(pv + d0) = xv;
+        }
+    }
   }
 }
 
@@ -351,6 +401,36 @@ __global__ __launch_bounds__(NTB) void bwd_dq_kernel(const float* __restrict__ a
   st16(dq + i * 8, out);
 }
 
+// dK = scale * sum of the partial sums, dV = sum, when the head group of a
+// key block was split across workgroups (fixed order: deterministic).
+template <typename T>
+__global__ __launch_bounds__(NTB) void bwd_kv_reduce_kernel(const float* __restrict__ pk,
+                                                            const float* __restrict__ pv,
+                                                            uint16_t* __restrict__ dk,
+                                                            uint16_t* __restrict__ dv, size_t n4,
+                                                            int parts, float scale) {
+  const size_t i = (size_t)blockIdx.x * NTB + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 sk = *reinterpret_cast<const f32x4*>(pk + i * 4);
+  f32x4 sv = *reinterpret_cast<const f32x4*>(pv + i * 4);
+  for (int g = 1; g < parts; ++g) {
+    const f32x4 xk = *reinterpret_cast<const f32x4*>(pk + (size_t)g * n4 * 4 + i * 4);
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(pv + (size_t)g * n4 * 4 + i * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sk[j] += xk[j];
+      sv[j] += xv[j];
+    }
+  }
+  u32x2 ok, ov;
+  ok[0] = pack2<T>(sk[0] * scale, sk[1] * scale);
+  ok[1] = pack2<T>(sk[2] * scale, sk[3] * scale);
+  ov[0] = pack2<T>(sv[0], sv[1]);
+  ov[1] = pack2<T>(sv[2], sv[3]);
+  *reinterpret_cast<u32x2*>(dk + i * 4) = ok;
+  *reinterpret_cast<u32x2*>(dv + i * 4) = ov;
+}
+
 BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   BwdArgs a;
   a.q = static_cast<const uint16_t*>(t.q);
@@ -364,6 +444,9 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.dv = static_cast<uint16_t*>(t.dv);
   a.dq_acc = t.dq_acc;
   a.delta = t.delta;
+  a.dk_part = t.dk_part;
+  a.dv_part = t.dv_part;
+  a.gsplit = bwd_group_split(p);
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.G = p.G;
@@ -392,7 +475,7 @@ template <typename T, int D>
 hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const BwdArgs a = make_args(p, t);
   if (a.n_kblocks == 0 || a.n_bk == 0) return hipSuccess;
-  dim3 grid((unsigned)(a.n_kblocks * a.n_bk));
+  dim3 grid((unsigned)(a.n_kblocks * a.n_bk * a.gsplit));
   if (p.causal)
     hipLaunchKernelGGL((bwd_main_kernel<T, D, true>), grid, dim3(NTB), 0, stream, a);
   else
@@ -403,11 +486,23 @@ hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
 template <typename T>
 hipError_t dq_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const size_t n8 = (size_t)p.B * p.Hq * p.Nq * p.d / 8;
-  if (n8 == 0) return hipSuccess;
-  dim3 grid((unsigned)((n8 + NTB - 1) / NTB));
-  hipLaunchKernelGGL((bwd_dq_kernel<T>), grid, dim3(NTB), 0, stream, t.dq_acc,
-                     static_cast<uint16_t*>(t.dq), n8, p.scale);
-  return hipGetLastError();
+  if (n8 > 0) {
+    dim3 grid((unsigned)((n8 + NTB - 1) / NTB));
+    hipLaunchKernelGGL((bwd_dq_kernel<T>), grid, dim3(NTB), 0, stream, t.dq_acc,
+                       static_cast<uint16_t*>(t.dq), n8, p.scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int parts = bwd_group_split(p);
+  const size_t n4 = (size_t)p.B * p.Hkv * p.Nkv * p.d / 4;
+  if (parts > 1 && n4 > 0) {
+    dim3 grid((unsigned)((n4 + NTB - 1) / NTB));
+    hipLaunchKernelGGL((bwd_kv_reduce_kernel<T>), grid, dim3(NTB), 0, stream, t.dk_part,
+                       t.dv_part, static_cast<uint16_t*>(t.dk), static_cast<uint16_t*>(t.dv), n4,
+                       parts, p.scale);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace

@@ -39,6 +39,8 @@ struct BwdPtrs {
   void* dv;
   float* dq_acc;     // [B, Hq, Nq, d] float32, in the workspace
   float* delta;      // [B, Hq, Nq]    float32, in the workspace
+  float* dk_part;    // [gsplit, B, Hkv, Nkv, d] float32 partial sums, or NULL
+  float* dv_part;    //   (present only when the head group is split)
 };
 
 // Decode (N_q == 1) split-KV geometry, shared by the workspace size and the
@@ -50,6 +52,10 @@ struct DecodeSplit {
 DecodeSplit decode_split(const Problem& p);
 size_t decode_workspace_bytes(const Problem& p);
 size_t bwd_workspace_bytes(const Problem& p);
+// Number of workgroups that share the query heads of one key block in the
+// backward (1 unless there are too few key blocks to fill the GPU); always a
+// divisor of G.
+int bwd_group_split(const Problem& p);
 
 // Launchers: each enqueues its kernel(s) on `stream` and returns the
 // hipError_t of the launch.

@@ -54,9 +54,18 @@ def test_workspace_sizes():
     rows = ws // (129 * 4)
     assert rows % (16 * 32) == 0
     # Backward: float32 dQ accumulator + float32 row terms, linear in N.
-    for B, Hq, Hkv, N, d in [(1, 32, 32, 4096, 128), (2, 16, 16, 1024, 64), (4, 32, 1, 2048, 128)]:
+    for B, Hq, Hkv, N, d in [(1, 32, 32, 4096, 128), (2, 16, 16, 1024, 64), (4, 32, 8, 2048, 128)]:
         want = _align(B * Hq * N * d * 4) + _align(B * Hq * N * 4)
         assert lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) == want
+    # MQA with few key blocks: the head group is split over s workgroups, which
+    # adds float32 partial dK and dV planes (s of each), s a divisor of G.
+    B, Hq, Hkv, N, d = 4, 32, 1, 2048, 128
+    base = _align(B * Hq * N * d * 4) + _align(B * Hq * N * 4)
+    extra = lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) - base
+    plane = B * Hkv * N * d * 4
+    assert extra > 0 and extra % (2 * plane) == 0
+    s = extra // (2 * plane)
+    assert s > 1 and (Hq // Hkv) % s == 0
     assert lib.fa_bwd_workspace_size(1, 1, 1, 10, 10, 64, fa.FA_F32) == 0
     # Invalid problems report 0.
     assert lib.fa_bwd_workspace_size(1, 3, 2, 10, 10, 64, fa.FA_BF16) == 0
