@@ -48,6 +48,8 @@ int check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int dt, bool* em
   const long long big = 1LL << 31;
   if ((long long)B * Hq * (((long long)Nq + 127) / 128) >= big) return FA_ERR_UNSUPPORTED;
   if ((long long)B * Hq * Nq >= big || (long long)B * Hkv * Nkv >= big) return FA_ERR_UNSUPPORTED;
+  // One head's K (or V) is addressed with 32-bit byte offsets.
+  if ((long long)Nkv * d * 4 >= big) return FA_ERR_UNSUPPORTED;
   *empty = (B == 0 || Hq == 0 || Nq == 0);
   return FA_OK;
 }

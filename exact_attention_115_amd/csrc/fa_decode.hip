@@ -68,8 +68,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
   const int key_end = min(a.Nkv, key_begin + a.keys_per_split);
   const int n_tiles = key_end > key_begin ? (key_end - key_begin + BC - 1) / BC : 0;
 
-  const uint16_t* kbase = a.k + ((size_t)bk * a.Nkv) * D;
-  const uint16_t* vbase = a.v + ((size_t)bk * a.Nkv) * D;
+  // Buffer resources over this split's keys: reads past key_end return zero.
+  const size_t split_off = ((size_t)bk * a.Nkv + key_begin) * D;
+  const uint32_t split_bytes = (uint32_t)max(key_end - key_begin, 0) * D * 2u;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + split_off, split_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + split_off, split_bytes);
 
   V8 qf[KC];
 #pragma unroll
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
 
   KVTileRegs<D> regs;
   if (n_tiles > 0) {
-    load_kv_tile<D>(regs, kbase, vbase, key_begin, key_end, tid);
+    load_kv_tile<D>(regs, krs, vrs, 0, 0, tid);
     store_kv_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
   }
   __syncthreads();
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
   for (int j = 0; j < n_tiles; ++j) {
     const bool more = j + 1 < n_tiles;
     const int key0 = key_begin + j * BC;
-    if (more) load_kv_tile<D>(regs, kbase, vbase, key0 + BC, key_end, tid);
+    if (more) load_kv_tile<D>(regs, krs, vrs, (j + 1) * BC, (j + 1) * BC, tid);
 
     const uint16_t* ks = smem + stage * L::STAGE;
     const uint16_t* vt = ks + L::K_ELEMS;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = zero16();
-        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RS + h * 8;
+        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RSK + h * 8;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
           s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(krow + kc * 16)), qf[kc], s[kb]);
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
         float pv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-        const V8 va = load_vt_operand<T, L::RS>(vt, h, c, ch * 16, wave * 32);
+        const V8 va = load_vt_operand<T, L::RSV>(vt, h, c, ch * 16, wave * 32);
         oacc = T::mfma(va, pack8<T>(pv), oacc);
       }
     }

@@ -19,9 +19,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct BF16 {
   using vec8 = bf16x8;
+  using vec2 = bf16x2;
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -36,6 +40,7 @@ struct BF16 {
 
 struct F16 {
   using vec8 = f16x8;
+  using vec2 = f16x2;
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -48,10 +53,14 @@ struct F16 {
   }
 };
 
-// Pack two floats into one 32-bit word of two 16-bit elements (lo first).
+// Pack two floats into one 32-bit word of two 16-bit elements (lo first),
+// rounding to nearest even: one v_cvt_pk_{bf16,f16}_f32 on gfx950.
 template <typename T>
 __device__ inline uint32_t pack2(float lo, float hi) {
-  return static_cast<uint32_t>(T::from_float(lo)) | (static_cast<uint32_t>(T::from_float(hi)) << 16);
+  f32x2 x;
+  x[0] = lo;
+  x[1] = hi;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, typename T::vec2));
 }
 
 // Eight floats -> one 8-element 16-bit matrix-core operand.

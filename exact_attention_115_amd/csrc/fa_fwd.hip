@@ -23,10 +23,23 @@
 // * O^T = V^T P^T keeps the output accumulator lane = query as well, so the
 //   per-row rescale is lane-local. V stays row-major in LDS; its transpose is
 //   taken by the gfx950 transposed LDS read (see fa_tile.h).
-// * K and V^T tiles are double-buffered in LDS; the global loads of tile j+1
-//   are issued before the matrix-core work of tile j, one barrier per tile.
+// * K and V tiles are double-buffered in LDS, K one tile ahead of V: while
+//   tile j is exponentiated and multiplied by V, the matrix cores already
+//   compute the scores of tile j + 1 (software pipelining inside each wave),
+//   and the global loads of K tile j + 2 and V tile j + 1 are in flight; one
+//   barrier per tile.
 // * Exponentials use exp2 with log2(e) folded into the scale; the LSE is
 //   converted back to natural-log units at the end.
+// * Few vector-ALU operations per score (the matrix cores outrun them): P is
+//   rounded to 16 bits once per tile (one packed conversion per two scores),
+//   while the row sum l adds the unrounded float32 values, so the LSE keeps
+//   float32 accuracy. The running maximum is not recomputed for every tile:
+//   the tile's exponentials are first taken against the maximum held so
+//   far, and only when their sum in some row exceeds kSumLimit (or the row
+//   had no maximum yet) is the tile's true maximum found, U and l rescaled
+//   by exp(m_old - m_new) and the exponentials redone. Every U and l stay
+//   relative to the same m, so O = U / l and LSE = m + ln l are unchanged,
+//   and P stays below kSumLimit.
 #include <math.h>
 
 #include "fa_device.h"
@@ -36,11 +49,12 @@
 namespace fa {
 namespace {
 
-constexpr int BR = 128;     // query rows per workgroup
+constexpr int BR = 128;  // query rows per workgroup
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
-// Growth of the row maximum (log2 units) tolerated before rescaling.
-constexpr float kRescaleSlack = 8.0f;
+// Largest per-lane sum of a tile's exponentials accepted without moving the
+// running maximum (bounds every P value; fits bf16 and fp16).
+constexpr float kSumLimit = 1024.0f;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -48,42 +62,167 @@ struct FwdArgs {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int Hq, G, Nq, Nkv, n_qtiles, n_bh;
+  int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
   float scale_log2;
 };
 
+struct TileId {
+  int qt, b, hq;
+};
+
+// Workgroup w -> (query tile, batch, query head). Heaviest (last, under the
+// causal mask) query tiles go first. Workgroups are handed to the 8 XCDs
+// round-robin (w % 8); when the key/value heads divide evenly over the XCDs,
+// every query tile of the query heads sharing one key/value head is kept on
+// one XCD so that head's K and V are reused from that XCD's L2.
+__device__ inline TileId tile_of(int w, const FwdArgs& a) {
+  TileId t;
+  const int units = a.B * a.Hkv;
+  if ((units & 7) == 0) {
+    const int xcd = w & 7;
+    const int j = w >> 3;
+    const int per_level = (units >> 3) * a.G;  // workgroups per tile row, per XCD
+    t.qt = a.n_qtiles - 1 - j / per_level;
+    const int rem = j % per_level;
+    const int u = xcd + 8 * (rem / a.G);
+    t.b = u / a.Hkv;
+    t.hq = (u % a.Hkv) * a.G + rem % a.G;
+  } else {
+    const int n_bh = a.B * a.Hq;
+    t.qt = a.n_qtiles - 1 - w / n_bh;
+    const int bh = w % n_bh;
+    t.b = bh / a.Hq;
+    t.hq = bh % a.Hq;
+  }
+  return t;
+}
+
+// S^T = K Q^T for the 64 keys of the K tile at ks (DMA layout; kb0, kb1:
+// this lane's k_read_base for even and odd kc): two 32-key blocks,
+// accumulator r of block kb holds key kb * 32 + acc_key(h, r) of this lane's
+// query row.
+template <typename T, int D>
+__device__ inline void qk_tile(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
+                               const typename T::vec8* qf, f32x16* s) {
+  constexpr int RB = DmaTile<D>::RB;
+  constexpr int KC = D / 16;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint8_t* p = ks + ((kc & 1) ? kb1 : kb0) + kb * 32 * RB + (kc >> 1) * 1024;
+      s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), qf[kc], s[kb]);
+    }
+  }
+}
+
+// P = exp2(S * scale_log2 - m) rounded to 16 bits, pk[4 ch + t] holding the
+// keys 16 ch + 8 h + 2t, +1 of this lane's row (the B operand of chunk ch of
+// O^T += V^T P^T); returns this lane's sum of the unrounded values.
+template <typename T>
+__device__ inline float exp_tile(const f32x16* s, float sl2, float m, uint32_t* pk) {
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7)], sl2, -m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7) + 1], sl2, -m));
+    pk[i] = pack2<T>(p0, p1);
+    psum += p0 + p1;
+  }
+  return psum;
+}
+
+// The next tile's scores S' = K' Q^T (ks: that tile's K) computed alongside
+// this tile's exponentials (exp_tile on s): the D / 8 matrix-core products
+// and the 16 pairs of exponentials are issued in alternation (one or two
+// pairs per product), each product's
+// K fragment read from LDS two steps ahead, with scheduling fences between
+// the steps, so the wave keeps issuing vector work while its products run.
+template <typename T, int D>
+__device__ inline float qk_next_with_exp(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
+                                         const typename T::vec8* qf, f32x16* sn, const f32x16* s,
+                                         float sl2, float m, uint32_t* pk) {
+  constexpr int RB = DmaTile<D>::RB;
+  constexpr int N = D / 8;  // products: kb = i % 2, kc = i / 2
+  auto kfrag = [&](int i) {
+    const int kb = i & 1, kc = i >> 1;
+    return *reinterpret_cast<const u32x4*>(ks + ((kc & 1) ? kb1 : kb0) + kb * 32 * RB +
+                                           (kc >> 1) * 1024);
+  };
+  sn[0] = zero16();
+  sn[1] = zero16();
+  u32x4 f0 = kfrag(0), f1 = kfrag(1);
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    u32x4 f2 = f0;
+    if (i + 2 < N) f2 = kfrag(i + 2);
+    sn[i & 1] = T::mfma(as_vec8<T>(f0), qf[i >> 1], sn[i & 1]);
+#pragma unroll
+    for (int e = i * 16 / N; e < (i + 1) * 16 / N; ++e) {  // pairs of exponentials
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[e >> 3][2 * (e & 7)], sl2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e >> 3][2 * (e & 7) + 1], sl2, -m));
+      pk[e] = pack2<T>(p0, p1);
+      psum += p0 + p1;
+    }
+    // Keep the running sum in step (otherwise its adds drift to the end).
+    asm volatile("" : "+v"(psum));
+    __builtin_amdgcn_sched_barrier(0);
+    f0 = f1;
+    f1 = f2;
+  }
+  return psum;
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
-  using L = KVTileLds<D>;
   using V8 = typename T::vec8;
   constexpr int KC = D / 16;  // k-chunks of the QK^T contraction
   constexpr int OD = D / 32;  // 32-wide output column blocks
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+  // Two K tile buffers, then two V tile buffers, filled by direct
+  // global -> LDS loads. K is staged one tile ahead of V: while the scores of
+  // tile j are exponentiated, the matrix cores already compute the scores of
+  // tile j + 1.
+  // Separate arrays (and a tile loop unrolled by two, so every access names
+  // its buffer statically) let the compiler see that a tile's operand reads
+  // never touch the buffers the in-flight loads are filling, so it does not
+  // make the reads wait for those loads.
+  constexpr int TB = DmaTile<D>::BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TB];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int c = lane & 31;
 
-  // Heaviest (last) query tiles first so the causal tail is short.
-  const int w = blockIdx.x;
-  const int qt = a.n_qtiles - 1 - w / a.n_bh;
-  const int bh = w % a.n_bh;
-  const int b = bh / a.Hq;
-  const int hq = bh % a.Hq;
-  const int Hkv = a.Hq / a.G;
+  const TileId id = tile_of(blockIdx.x, a);
+  const int qt = id.qt;
+  const int b = id.b;
+  const int hq = id.hq;
   const int hkv = hq / a.G;
   const int Nq = a.Nq, Nkv = a.Nkv;
   const int offset = Nkv - Nq;
+  const size_t bh = (size_t)b * a.Hq + hq;
 
   const int q0 = qt * BR + wave * 32;  // first query row of this wave
   const int qrow = q0 + c;             // the row this lane owns
 
-  const uint16_t* qptr = a.q + ((size_t)bh * Nq) * D;
-  const uint16_t* kbase = a.k + ((size_t)(b * Hkv + hkv) * Nkv) * D;
-  const uint16_t* vbase = a.v + ((size_t)(b * Hkv + hkv) * Nkv) * D;
+  const uint16_t* qptr = a.q + bh * Nq * D;
+  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * Nkv * D;
+  const uint32_t kv_bytes = (uint32_t)Nkv * D * 2u;
+  const uint16_t* const khead = a.k + kv_off;
+  const uint16_t* const vhead = a.v + kv_off;
+  const uint32_t k_src = k_dma_src<D>(wave, lane);
+  const uint32_t v_src = v_dma_src<D>(wave, lane);
+  const uint32_t kr0 = k_read_base<D>(h, c, 0);
+  const uint32_t kr1 = k_read_base<D>(h, c, 1);
+  const uint32_t vr = v_read_base<D>(h, c);
 
   // Q^T as the B operand: lane holds Q[qrow][16 kc + 8h .. +7].
   V8 qf[KC];
@@ -91,124 +230,128 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   for (int kc = 0; kc < KC; ++kc)
     qf[kc] = as_vec8<T>(qrow < Nq ? ld16(qptr + (size_t)qrow * D + kc * 16 + h * 8) : zero_u32x4());
 
-  // Key tiles this workgroup needs.
+  // Key tiles this workgroup stages, and the ones this wave computes (the
+  // wave's rows may stop seeing keys earlier under the causal mask).
   const int kv_tiles = (Nkv + BC - 1) / BC;
   int n_tiles = kv_tiles;
   if (CAUSAL) {
     const int last_key = min(Nq, (qt + 1) * BR) - 1 + offset;
     n_tiles = last_key < 0 ? 0 : min(kv_tiles, last_key / BC + 1);
   }
-  // Last key any row of this wave may see (wave-uniform).
-  const int wave_last_row = min(Nq - 1, q0 + 31);
-  const int wave_last_key = CAUSAL ? wave_last_row + offset : Nkv - 1;
-  const bool wave_has_rows = q0 < Nq;
+  const int wave_last_key = CAUSAL ? min(Nq - 1, q0 + 31) + offset : Nkv - 1;
+  const int n_w = (q0 >= Nq || wave_last_key < 0) ? 0 : min(n_tiles, wave_last_key / BC + 1);
 
   f32x16 oacc[OD];
 #pragma unroll
   for (int od = 0; od < OD; ++od) oacc[od] = zero16();
   float m_run = -INFINITY;  // running max of scaled scores, log2 units
   float l_run = 0.0f;       // this half-wave's share of the running sum
+  const float sl2 = a.scale_log2;
 
-  KVTileRegs<D> regs;
+  constexpr int KS = DmaTile<D>::K_STEP, VS = DmaTile<D>::V_STEP;
   if (n_tiles > 0) {
-    load_kv_tile<D>(regs, kbase, vbase, 0, Nkv, tid);
-    store_kv_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
+    dma_tile<D>(kbuf0, khead, kv_bytes, 0, wave, k_src, KS);
+    dma_tile<D>(vbuf0, vhead, kv_bytes, 0, wave, v_src, VS);
+    if (n_tiles > 1) dma_tile<D>(kbuf1, khead, kv_bytes, BC, wave, k_src, KS);
   }
   __syncthreads();
 
-  int stage = 0;
-  for (int j = 0; j < n_tiles; ++j) {
-    const bool more = j + 1 < n_tiles;
-    if (more) load_kv_tile<D>(regs, kbase, vbase, (j + 1) * BC, Nkv, tid);
+  // Scores of the tile being exponentiated and of the next one; the two
+  // arrays swap roles every tile (the tile loop is unrolled by two).
+  f32x16 sa[2], sb[2];
+  if (n_w > 0) qk_tile<T, D>(kbuf0, kr0, kr1, qf, sa);
 
-    const uint16_t* ks = smem + stage * L::STAGE;
-    const uint16_t* vt = ks + L::K_ELEMS;
+  // Loads in flight during tile j: K of tile j + 2 into the buffer of K tile
+  // j (last read for the scores computed during tile j - 1) and V of tile
+  // j + 1 into the buffer of V tile j - 1; every wave passed the barrier
+  // that ended tile j - 1, so neither buffer is still being read.
+  auto issue_loads = [&](int j, uint8_t* kdst, uint8_t* vdst) {
+    if (j + 2 < n_tiles) dma_tile<D>(kdst, khead, kv_bytes, (j + 2) * BC, wave, k_src, KS);
+    if (j + 1 < n_tiles) dma_tile<D>(vdst, vhead, kv_bytes, (j + 1) * BC, wave, v_src, VS);
+  };
+
+  // Tile j with scores s: mask, exponentiate while the matrix cores compute
+  // the next tile's scores into sn (on a wave's last tile those are
+  // computed from whatever the K buffer holds and never used), fold into
+  // (m, l, U).
+  auto step = [&](int j, f32x16* s, f32x16* sn, const uint8_t* knext, const uint8_t* vt) {
     const int key0 = j * BC;
-
-    if (wave_has_rows && key0 <= wave_last_key) {
-      // S^T for keys key0 + [0, 64): two 32-key blocks.
-      f32x16 s[2];
+    // Mask keys past the end and, when causal, keys after the row's limit.
+    const bool need_mask = (key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nkv - 1, qrow + offset) : Nkv - 1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
-        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RS + h * 8;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const V8 ka = as_vec8<T>(*reinterpret_cast<const u32x4*>(krow + kc * 16));
-          s[kb] = T::mfma(ka, qf[kc], s[kb]);
-        }
-      }
-      // Mask keys past the end and, when causal, keys after the row's limit.
-      const bool need_mask = (key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Nkv - 1, qrow + offset) : Nkv - 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
-      }
-      // Online softmax update ([KB] §04) in log2 units. The running
-      // maximum is only moved (and U, l rescaled) when some row of the wave
-      // sees a score more than kRescaleSlack above it; otherwise the stale
-      // maximum is kept. Both U and l are always relative to the same m, so
-      // O = U / l and LSE = m + log l are unchanged; p stays <= 2^slack.
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
+    }
+    uint32_t pk[16];
+    float psum =
+        qk_next_with_exp<T, D>(knext, kr0, kr1, qf, sn, s, sl2, m_run, pk);
+    if (__builtin_expect(__any(!(psum <= kSumLimit)), 0)) {
+      // Move the maximum to the true running maximum and redo the tile.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx)) * a.scale_log2;
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
+      mx = fmaxf(mx, swap_halves(mx)) * sl2;
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-        for (int od = 0; od < OD; ++od)
+      for (int od = 0; od < OD; ++od)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.scale_log2, -m_use));
-          s[kb][r] = p;
-          psum += p;
-        }
-      l_run += psum;
-
-      // O^T += V^T P^T over four 16-key chunks.
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-        const V8 pf = pack8<T>(pv);
-#pragma unroll
-        for (int od = 0; od < OD; ++od) {
-          const V8 va = load_vt_operand<T, L::RS>(vt, h, c, ch * 16, od * 32);
-          oacc[od] = T::mfma(va, pf, oacc[od]);
-        }
-      }
+        for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
+      m_run = m_new;
+      psum = exp_tile<T>(s, sl2, (m_new == -INFINITY) ? 0.0f : m_new, pk);
     }
+    l_run += psum;
 
-    if (more) {
-      uint16_t* nks = smem + (stage ^ 1) * L::STAGE;
-      store_kv_tile<D>(regs, nks, nks + L::K_ELEMS, tid);
+    // O^T += V^T P^T over four 16-key chunks.
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      u32x4 w;
+      w[0] = pk[4 * ch + 0];
+      w[1] = pk[4 * ch + 1];
+      w[2] = pk[4 * ch + 2];
+      w[3] = pk[4 * ch + 3];
+      const V8 pf = as_vec8<T>(w);
+#pragma unroll
+      for (int od = 0; od < OD; ++od)
+        oacc[od] = T::mfma(load_vt_dma<T, D>(vt, vr, ch, od), pf, oacc[od]);
     }
+  };
+
+  // Every wave runs n_tiles (loads, barrier) rounds and computes its first
+  // n_w tiles; the barrier also waits for the wave's own loads.
+  // Tile j (even) reads K tile j + 1 from kbuf1 and V tile j from vbuf0
+  // while K tile j + 2 loads into kbuf0 and V tile j + 1 into vbuf1; odd
+  // tiles the other way round.
+  for (int j = 0; j < n_w; j += 2) {
+    issue_loads(j, kbuf0, vbuf1);
+    step(j, sa, sb, kbuf1, vbuf0);
     __syncthreads();
-    stage ^= 1;
+    if (j + 1 < n_w) {
+      issue_loads(j + 1, kbuf1, vbuf0);
+      step(j + 1, sb, sa, kbuf0, vbuf1);
+      __syncthreads();
+    }
+  }
+  for (int j = n_w; j < n_tiles; ++j) {
+    if (j & 1)
+      issue_loads(j, kbuf1, vbuf0);
+    else
+      issue_loads(j, kbuf0, vbuf1);
+    __syncthreads();
   }
 
   // Epilogue: O = U / l, LSE = m + ln l (natural log).
   const float l = l_run + swap_halves(l_run);
   if (qrow < Nq) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t* orow = a.o + ((size_t)bh * Nq + qrow) * D;
+    uint16_t* orow = a.o + (bh * Nq + qrow) * D;
 #pragma unroll
     for (int od = 0; od < OD; ++od)
 #pragma unroll
@@ -218,8 +361,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
         out[1] = pack2<T>(oacc[od][4 * g + 2] * inv, oacc[od][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + od * 32 + g * 8 + h * 4) = out;
       }
-    if (h == 0)
-      a.lse[(size_t)bh * Nq + qrow] = l > 0.0f ? (m_run + __log2f(l)) * LN2 : -INFINITY;
+    if (h == 0) a.lse[bh * Nq + qrow] = l > 0.0f ? (m_run + __log2f(l)) * LN2 : -INFINITY;
   }
 }
 
@@ -231,14 +373,15 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) 
   a.v = static_cast<const uint16_t*>(t.v);
   a.o = static_cast<uint16_t*>(t.o);
   a.lse = t.lse;
+  a.B = p.B;
   a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
   a.G = p.G;
   a.Nq = p.Nq;
   a.Nkv = p.Nkv;
   a.n_qtiles = (p.Nq + BR - 1) / BR;
-  a.n_bh = p.B * p.Hq;
   a.scale_log2 = p.scale * LOG2E;
-  dim3 grid(a.n_qtiles * a.n_bh);
+  dim3 grid(a.n_qtiles * p.B * p.Hq);
   if (p.causal)
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), grid, dim3(NT), 0, stream, a);
   else

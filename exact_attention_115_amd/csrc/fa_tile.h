@@ -1,17 +1,24 @@
 // K / V tile staging for the forward and decode kernels: a tile of BC = 64
-// keys is read from global memory with 16-byte loads into registers, then
-// written to LDS row-major, K[key][dim] and V[key][dim], each row padded by
-// 32 bytes. The pad puts consecutive rows 8 banks apart, so neither the
-// 16-byte row reads of K nor the transposed 8-byte reads of V (below) hit the
-// same bank twice in one access group.
+// keys is read from global memory with 16-byte buffer loads into registers,
+// then written to LDS row-major, K[key][dim] and V[key][dim], with padded
+// rows so that the matrix-core operand reads below do not hit the same LDS
+// bank twice in one access group:
+// * K rows are read 16 bytes per lane, 16 consecutive rows per access
+//   group; a 16-byte pad puts consecutive rows 4 banks apart, so the 16 rows
+//   cover all 64 banks once.
+// * V is consumed as the A operand of O^T += V^T P^T, i.e. eight consecutive
+//   KEYS of one dim per lane, which is a column of the row-major tile.
+//   gfx950's transposed LDS read (ds_read_b64_tr_b16) delivers exactly that:
+//   within each group of 16 lanes, the lanes' 4-element row chunks form a
+//   16 x 4 matrix M (row = source lane) and result lane i receives
+//   M[4k + i/4][i % 4], k = 0..3. One such group reads 32 bytes from each of
+//   4 consecutive rows; a 32-byte pad puts those rows 8 banks apart.
+//   vt_addr() gives each lane the row chunk to point at so that lane (h, c)
+//   receives V[key0 + 8h + 4s + k][dim0 + c], k = 0..3, for half s = 0, 1.
 //
-// V is consumed as the A operand of O^T += V^T P^T, i.e. eight consecutive
-// KEYS of one dim per lane, which is a column of the row-major tile. gfx950's
-// transposed LDS read (ds_read_b64_tr_b16) delivers exactly that: within each
-// group of 16 lanes, the lanes' 4-element row chunks form a 16 x 4 matrix M
-// (row = source lane) and result lane i receives M[4k + i/4][i % 4], k = 0..3.
-// vt_addr() gives each lane the row chunk to point at so that lane (h, c)
-// receives V[key0 + 8h + 4s + k][dim0 + c], k = 0..3, for half s = 0, 1.
+// Global reads go through a buffer resource whose size is the head's K (or
+// V) extent: reads past the last key return zero without a branch, and the
+// caller masks those keys to -inf.
 #pragma once
 
 #include "fa_device.h"
@@ -25,11 +32,22 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 struct KVTileLds {
-  static constexpr int RS = D + 16;  // row stride (elements) of both K and V
-  static constexpr int K_ELEMS = BC * RS;
-  static constexpr int V_ELEMS = BC * RS;
+  static constexpr int RSK = D + 8;   // K row stride (elements)
+  static constexpr int RSV = D + 16;  // V row stride (elements)
+  static constexpr int K_ELEMS = BC * RSK;
+  static constexpr int V_ELEMS = BC * RSV;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
 };
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled; reads at or
+// past `bytes` return zero).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
 
 // Global loads of one K/V tile held in registers between issue and LDS write.
 template <int D>
@@ -39,31 +57,148 @@ struct KVTileRegs {
   u32x4 v[CH];
 };
 
+// Byte offset, inside a head, of chunk i of thread tid for the tile at key 0
+// (add key0 * D * 2 for the tile at key0); also the chunk's LDS position.
 template <int D>
-__device__ inline void load_kv_tile(KVTileRegs<D>& r, const uint16_t* __restrict__ kbase,
-                                    const uint16_t* __restrict__ vbase, int key0, int key_end,
-                                    int tid) {
+__device__ inline uint32_t tile_chunk_off(int tid, int i) {
+  const int id = tid + NT * i;
+  return (uint32_t)((id / (D / 8)) * D + (id % (D / 8)) * 8) * 2u;
+}
+
+template <int D>
+__device__ inline void load_k_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t kr, int key0, int tid) {
+  const uint32_t base = (uint32_t)key0 * D * 2u;
+#pragma unroll
+  for (int i = 0; i < KVTileRegs<D>::CH; ++i) r.k[i] = buf_ld16(kr, base + tile_chunk_off<D>(tid, i));
+}
+
+template <int D>
+__device__ inline void load_v_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t vr, int key0, int tid) {
+  const uint32_t base = (uint32_t)key0 * D * 2u;
+#pragma unroll
+  for (int i = 0; i < KVTileRegs<D>::CH; ++i) r.v[i] = buf_ld16(vr, base + tile_chunk_off<D>(tid, i));
+}
+
+// K tile at key k0 and V tile at key v0.
+template <int D>
+__device__ inline void load_kv_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
+                                    __amdgpu_buffer_rsrc_t vr, int k0, int v0, int tid) {
+  load_k_tile<D>(r, kr, k0, tid);
+  load_v_tile<D>(r, vr, v0, tid);
+}
+
+template <int D>
+__device__ inline void store_k_tile(const KVTileRegs<D>& r, uint16_t* ks, int tid) {
 #pragma unroll
   for (int i = 0; i < KVTileRegs<D>::CH; ++i) {
     const int id = tid + NT * i;
-    const int key = id / (D / 8), dc = id % (D / 8);
-    const bool in = key0 + key < key_end;
-    const size_t off = (size_t)(key0 + key) * D + dc * 8;
-    r.k[i] = in ? ld16(kbase + off) : zero_u32x4();
-    r.v[i] = in ? ld16(vbase + off) : zero_u32x4();
+    *reinterpret_cast<u32x4*>(ks + (id / (D / 8)) * KVTileLds<D>::RSK + (id % (D / 8)) * 8) = r.k[i];
+  }
+}
+
+template <int D>
+__device__ inline void store_v_tile(const KVTileRegs<D>& r, uint16_t* vs, int tid) {
+#pragma unroll
+  for (int i = 0; i < KVTileRegs<D>::CH; ++i) {
+    const int id = tid + NT * i;
+    *reinterpret_cast<u32x4*>(vs + (id / (D / 8)) * KVTileLds<D>::RSV + (id % (D / 8)) * 8) = r.v[i];
   }
 }
 
 template <int D>
 __device__ inline void store_kv_tile(const KVTileRegs<D>& r, uint16_t* ks, uint16_t* vs, int tid) {
-  using L = KVTileLds<D>;
+  store_k_tile<D>(r, ks, tid);
+  store_v_tile<D>(r, vs, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS staging (gfx950 buffer_load ... lds): a 16-byte load
+// per lane, written by the hardware to LDS at M0 + 16 * lane, so one wave
+// instruction fills 1 KiB of LDS and no VGPRs hold the tile in between. Each
+// lane chooses which 16-byte chunk of the tile it fetches; the layouts below
+// keep every fetch a whole 64-byte run of a key row (coalesced) and every
+// matrix-core operand read below free of LDS bank conflicts.
+//
+// K tile: rows r = 16 m + u (u < 16), 16-byte chunks q of a row. Chunk q of
+// row r lives at byte
+//   m * 16 RB + (q / 4) * 1024 + u * 64 + ((q % 4) ^ (u / 4)) * 16,
+// i.e. each 64-byte run of a row in its own 64-byte slot, its four chunks
+// permuted by u / 4. The operand read (16 lanes read the same chunk of 16
+// rows u = 0..15) then touches every 16-byte bank group of a 256-byte bank
+// line exactly once.
+//
+// V tile: rows r = 4 R4 + t (t < 4). Chunk q of row r lives at byte
+//   R4 * 4 RB + (q / 4) * 256 + t * 64 + (q % 4) * 16,
+// i.e. 4 rows x 64 bytes per 256-byte block. A transposed read (16 lanes:
+// 4 consecutive rows x 32 bytes; 32 lanes: 4 rows x 64 bytes) stays inside
+// one such block and touches each bank once.
+template <int D>
+struct DmaTile {
+  static constexpr int RB = 2 * D;                  // bytes per key row
+  static constexpr int BYTES = BC * RB;             // bytes per tile
+  static constexpr int PER_WAVE = BYTES / 1024 / 4;  // 1 KiB DMA blocks per wave
+  static constexpr int K_STEP = 64;                 // source step between a wave's K blocks
+  static constexpr int V_STEP = 1024;               // source step between a wave's V blocks
+};
+
+// Tile-relative source byte of lane l's chunk in the wave's first K block
+// (block i of the wave adds i * K_STEP).
+template <int D>
+__device__ inline uint32_t k_dma_src(int wave, int l) {
+  using T = DmaTile<D>;
+  const int u = l >> 2, slot = l & 3;
+  return (uint32_t)((16 * wave + u) * T::RB + (slot ^ (u >> 2)) * 16);
+}
+
+// Same for V (block i adds i * V_STEP).
+template <int D>
+__device__ inline uint32_t v_dma_src(int wave, int l) {
+  using T = DmaTile<D>;
+  const int b = (T::PER_WAVE * wave) * 1024 + 16 * l;  // LDS byte of the wave's first block
+  const int r4 = b / (4 * T::RB), rem = b % (4 * T::RB);
+  const int q = 4 * (rem >> 8) + ((rem >> 4) & 3);
+  const int t = (rem >> 6) & 3;
+  return (uint32_t)((4 * r4 + t) * T::RB + q * 16);
+}
+
+// Issue this wave's DMA loads of one K (or V) tile: `tile` is the tile's LDS
+// base, `head` the global base of the head's K (or V), `head_bytes` its size,
+// `key0` the tile's first key. Reads past the head's end fill zeros.
+template <int D>
+__device__ inline void dma_tile(uint8_t* tile, const uint16_t* head, uint32_t head_bytes, int key0,
+                                int wave, uint32_t lane_src, int step) {
+  using T = DmaTile<D>;
 #pragma unroll
-  for (int i = 0; i < KVTileRegs<D>::CH; ++i) {
-    const int id = tid + NT * i;
-    const int key = id / (D / 8), dc = id % (D / 8);
-    *reinterpret_cast<u32x4*>(ks + key * L::RS + dc * 8) = r.k[i];
-    *reinterpret_cast<u32x4*>(vs + key * L::RS + dc * 8) = r.v[i];
+  for (int i = 0; i < T::PER_WAVE; ++i) {
+    const uint32_t start = (uint32_t)key0 * T::RB + (uint32_t)(i * step);
+    // Scalar arithmetic (min then subtract) keeps the resource in SGPRs.
+    const uint32_t left = head_bytes - __builtin_amdgcn_readfirstlane(min(head_bytes, start));
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(reinterpret_cast<const uint8_t*>(head) + start, left);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(tile + (wave * T::PER_WAVE + i) * 1024), 16,
+        lane_src, 0, 0, 0);
   }
+}
+
+// Per-lane byte offsets of the matrix-core operand reads.
+// K (A operand of S^T = K Q^T, lane (h, c) reads row kb * 32 + row_perm(c),
+// chunk 2 kc + h): byte = k_read_base(h, c, kc % 2) + kb * 32 RB + (kc / 2) * 1024.
+template <int D>
+__device__ inline uint32_t k_read_base(int h, int c, int parity) {
+  using T = DmaTile<D>;
+  const int u = row_perm(c) & 15;
+  return (uint32_t)((c >> 4) * 16 * T::RB + u * 64 + (((2 * parity + h) ^ (u >> 2)) << 4));
+}
+
+// V (transposed read of rows ch * 16 + 8h + 4s + j / 4, element columns
+// od * 32 + 16 (c / 16) + 4 (j % 4), j = c % 16):
+// byte = v_read_base(h, c) + (4 ch + s) * 4 RB + od * 256.
+template <int D>
+__device__ inline uint32_t v_read_base(int h, int c) {
+  using T = DmaTile<D>;
+  const int j = c & 15;
+  return (uint32_t)(8 * h * T::RB + (j >> 2) * 64 + (2 * (c >> 4) + ((j >> 1) & 1)) * 16 + 8 * (j & 1));
 }
 
 // Element offset, inside a V tile, of the 4-element row chunk lane (h, c)
@@ -88,6 +223,20 @@ __device__ inline typename T::vec8 load_vt_operand(const uint16_t* vs, int h, in
                                                    int dim0) {
   const s16x4 lo = ds_read_tr16(vs + vt_addr<RS>(h, c, key0, dim0, 0));
   const s16x4 hi = ds_read_tr16(vs + vt_addr<RS>(h, c, key0, dim0, 1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 x;
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+  x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+  return __builtin_bit_cast(typename T::vec8, x);
+}
+
+// The A operand V^T[dim0 + c][key0 + 8h .. +7] (dim0 = 32 od, key0 = 16 ch)
+// from a DMA-staged V tile (vt: its LDS base, vb: v_read_base).
+template <typename T, int D>
+__device__ inline typename T::vec8 load_vt_dma(const uint8_t* vt, uint32_t vb, int ch, int od) {
+  constexpr int RB = DmaTile<D>::RB;
+  const s16x4 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vb + (4 * ch) * 4 * RB + od * 256));
+  const s16x4 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(vt + vb + (4 * ch + 1) * 4 * RB + od * 256));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 x;
   x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];

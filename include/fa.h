@@ -31,7 +31,8 @@
  * dtypes: FA_F32 (forward only), FA_F16, FA_BF16. Outputs have the input
  *   dtype; all accumulation is float32; float32 -> 16-bit conversions round
  *   to nearest even.
- * Head dim d: 64 or 128.
+ * Head dim d: 64 or 128. Sizes: N_kv * d < 2^29 (one head's K or V under
+ *   2 GiB) and B * H * N < 2^31; larger problems return FA_ERR_UNSUPPORTED.
  * Pointers: device pointers, 16-byte aligned; the workspace 256-byte aligned.
  *   Outputs must not overlap inputs. Every output element is overwritten.
  * Ownership: the caller allocates and frees every buffer, including the
