@@ -133,44 +133,78 @@ __device__ inline float exp_tile(const f32x16* s, float sl2, float m, uint32_t* 
   return psum;
 }
 
-// The next tile's scores S' = K' Q^T (ks: that tile's K) computed alongside
-// this tile's exponentials (exp_tile on s): the D / 8 matrix-core products
-// and the 16 pairs of exponentials are issued in alternation (one or two
-// pairs per product), each product's
-// K fragment read from LDS two steps ahead, with scheduling fences between
-// the steps, so the wave keeps issuing vector work while its products run.
+// One step of the software pipeline, as a single interleaved instruction
+// stream (the three parts are independent of each other):
+//   * scores of tile i + 2:   sn = K Q^T         (kt: that K tile, D/8 products)
+//   * output of tile i:       U += V^T P^T        (vt: V tile i, pc: P of tile i,
+//                                                  D/8 products)
+//   * exponentials of tile i + 1: pn = 16-bit exp2(se * scale_log2 - m)
+// Matrix-core products alternate between the two products; every product's
+// LDS operands are read two products ahead; each product is followed by its
+// share of the exponentials; scheduling fences keep that order. Returns this
+// lane's sum of the (unrounded) exponentials.
 template <typename T, int D>
-__device__ inline float qk_next_with_exp(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
-                                         const typename T::vec8* qf, f32x16* sn, const f32x16* s,
-                                         float sl2, float m, uint32_t* pk) {
+__device__ inline float fused_tile(const uint8_t* kt, uint32_t kr0, uint32_t kr1,
+                                   const typename T::vec8* qf, f32x16* sn, const uint8_t* vt,
+                                   uint32_t vr, const uint32_t* pc, f32x16* oacc,
+                                   const f32x16* se, float sl2, float m, uint32_t* pn) {
+  using V8 = typename T::vec8;
   constexpr int RB = DmaTile<D>::RB;
-  constexpr int N = D / 8;  // products: kb = i % 2, kc = i / 2
-  auto kfrag = [&](int i) {
-    const int kb = i & 1, kc = i >> 1;
-    return *reinterpret_cast<const u32x4*>(ks + ((kc & 1) ? kb1 : kb0) + kb * 32 * RB +
+  constexpr int OD = D / 32;
+  constexpr int NQ = D / 8;   // score products: kb = q % 2, kc = q / 2
+  constexpr int NP = 4 * OD;  // output products: ch = p / OD, od = p % OD
+  static_assert(NQ == NP, "alternating products");
+  constexpr int NM = NQ + NP;
+  auto kfrag = [&](int q) {
+    const int kb = q & 1, kc = q >> 1;
+    return *reinterpret_cast<const u32x4*>(kt + ((kc & 1) ? kr1 : kr0) + kb * 32 * RB +
                                            (kc >> 1) * 1024);
   };
+  auto vfrag = [&](int p) { return load_vt_dma<T, D>(vt, vr, p / OD, p % OD); };
   sn[0] = zero16();
   sn[1] = zero16();
-  u32x4 f0 = kfrag(0), f1 = kfrag(1);
-  float psum = 0.0f;
+  u32x4 kf[NQ];
+  V8 vf[NP];
+  kf[0] = kfrag(0);
+  kf[1] = kfrag(1);
+  vf[0] = vfrag(0);
+  vf[1] = vfrag(1);
+  float psum = 0.0f, e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    u32x4 f2 = f0;
-    if (i + 2 < N) f2 = kfrag(i + 2);
-    sn[i & 1] = T::mfma(as_vec8<T>(f0), qf[i >> 1], sn[i & 1]);
-#pragma unroll
-    for (int e = i * 16 / N; e < (i + 1) * 16 / N; ++e) {  // pairs of exponentials
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[e >> 3][2 * (e & 7)], sl2, -m));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e >> 3][2 * (e & 7) + 1], sl2, -m));
-      pk[e] = pack2<T>(p0, p1);
+  for (int t = 0; t < NM; ++t) {
+    const int i = t >> 1;
+    if ((t & 1) == 0) {
+      if (i + 2 < NQ) kf[i + 2] = kfrag(i + 2);
+      sn[i & 1] = T::mfma(as_vec8<T>(kf[i]), qf[i >> 1], sn[i & 1]);
+    } else {
+      if (i + 2 < NP) vf[i + 2] = vfrag(i + 2);
+      const int ch = i / OD, od = i % OD;
+      u32x4 w;
+      w[0] = pc[4 * ch + 0];
+      w[1] = pc[4 * ch + 1];
+      w[2] = pc[4 * ch + 2];
+      w[3] = pc[4 * ch + 3];
+      oacc[od] = T::mfma(vf[i], as_vec8<T>(w), oacc[od]);
+    }
+    if constexpr (NM == 32) {  // half a pair of exponentials per product
+      const int e = t >> 1;
+      if ((t & 1) == 0) {
+        e0 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7)], sl2, -m));
+        e1 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7) + 1], sl2, -m));
+      } else {
+        pn[e] = pack2<T>(e0, e1);
+        psum += e0 + e1;
+      }
+    } else {  // one pair per product
+      const int e = t;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7)], sl2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7) + 1], sl2, -m));
+      pn[e] = pack2<T>(p0, p1);
       psum += p0 + p1;
     }
     // Keep the running sum in step (otherwise its adds drift to the end).
     asm volatile("" : "+v"(psum));
     __builtin_amdgcn_sched_barrier(0);
-    f0 = f1;
-    f1 = f2;
   }
   return psum;
 }
@@ -249,34 +283,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   const float sl2 = a.scale_log2;
 
   constexpr int KS = DmaTile<D>::K_STEP, VS = DmaTile<D>::V_STEP;
-  if (n_tiles > 0) {
-    dma_tile<D>(kbuf0, khead, kv_bytes, 0, wave, k_src, KS);
-    dma_tile<D>(vbuf0, vhead, kv_bytes, 0, wave, v_src, VS);
-    if (n_tiles > 1) dma_tile<D>(kbuf1, khead, kv_bytes, BC, wave, k_src, KS);
-  }
-  __syncthreads();
 
-  // Scores of the tile being exponentiated and of the next one; the two
-  // arrays swap roles every tile (the tile loop is unrolled by two).
-  f32x16 sa[2], sb[2];
-  if (n_w > 0) qk_tile<T, D>(kbuf0, kr0, kr1, qf, sa);
-
-  // Loads in flight during tile j: K of tile j + 2 into the buffer of K tile
-  // j (last read for the scores computed during tile j - 1) and V of tile
-  // j + 1 into the buffer of V tile j - 1; every wave passed the barrier
-  // that ended tile j - 1, so neither buffer is still being read.
-  auto issue_loads = [&](int j, uint8_t* kdst, uint8_t* vdst) {
-    if (j + 2 < n_tiles) dma_tile<D>(kdst, khead, kv_bytes, (j + 2) * BC, wave, k_src, KS);
-    if (j + 1 < n_tiles) dma_tile<D>(vdst, vhead, kv_bytes, (j + 1) * BC, wave, v_src, VS);
-  };
-
-  // Tile j with scores s: mask, exponentiate while the matrix cores compute
-  // the next tile's scores into sn (on a wave's last tile those are
-  // computed from whatever the K buffer holds and never used), fold into
-  // (m, l, U).
-  auto step = [&](int j, f32x16* s, f32x16* sn, const uint8_t* knext, const uint8_t* vt) {
+  // Mask keys past the end and, when causal, keys after the row's limit, in
+  // the scores s of tile j.
+  auto mask_tile = [&](int j, f32x16* s) {
     const int key0 = j * BC;
-    // Mask keys past the end and, when causal, keys after the row's limit.
     const bool need_mask = (key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset);
     if (need_mask) {
       const int lim = CAUSAL ? min(Nkv - 1, qrow + offset) : Nkv - 1;
@@ -286,11 +297,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r)
           if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
     }
-    uint32_t pk[16];
-    float psum =
-        qk_next_with_exp<T, D>(knext, kr0, kr1, qf, sn, s, sl2, m_run, pk);
+  };
+  // When the exponentials p of scores s (taken against m_run) summed to more
+  // than kSumLimit in some row: move the maximum to the true running maximum,
+  // rescale what U and l hold, and redo p. Returns the new sum.
+  auto fix_max = [&](const f32x16* s, uint32_t* p, float psum) {
     if (__builtin_expect(__any(!(psum <= kSumLimit)), 0)) {
-      // Move the maximum to the true running maximum and redo the tile.
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -305,45 +317,69 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
       m_run = m_new;
-      psum = exp_tile<T>(s, sl2, (m_new == -INFINITY) ? 0.0f : m_new, pk);
+      psum = exp_tile<T>(s, sl2, (m_new == -INFINITY) ? 0.0f : m_new, p);
     }
-    l_run += psum;
-
-    // O^T += V^T P^T over four 16-key chunks.
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      u32x4 w;
-      w[0] = pk[4 * ch + 0];
-      w[1] = pk[4 * ch + 1];
-      w[2] = pk[4 * ch + 2];
-      w[3] = pk[4 * ch + 3];
-      const V8 pf = as_vec8<T>(w);
-#pragma unroll
-      for (int od = 0; od < OD; ++od)
-        oacc[od] = T::mfma(load_vt_dma<T, D>(vt, vr, ch, od), pf, oacc[od]);
-    }
+    return psum;
   };
 
-  // Every wave runs n_tiles (loads, barrier) rounds and computes its first
-  // n_w tiles; the barrier also waits for the wave's own loads.
-  // Tile j (even) reads K tile j + 1 from kbuf1 and V tile j from vbuf0
-  // while K tile j + 2 loads into kbuf0 and V tile j + 1 into vbuf1; odd
-  // tiles the other way round.
-  for (int j = 0; j < n_w; j += 2) {
-    issue_loads(j, kbuf0, vbuf1);
-    step(j, sa, sb, kbuf1, vbuf0);
+  // Pipeline state entering step i: scores of tile i + 1 and the 16-bit P of
+  // tile i (already counted in l). Step i computes the scores of tile i + 2,
+  // U += P_i V_i and P of tile i + 1. The two score arrays and the two P
+  // arrays swap roles every step (the step loop is unrolled by two).
+  f32x16 sa[2], sb[2];
+  uint32_t pa[16], pb[16];
+
+  // Prologue: K tiles 0 and 1 and V tile 0; scores and P of tile 0, scores
+  // of tile 1 (whatever K buffer 1 holds when there is no tile 1); then K
+  // tile 2 into the buffer of K tile 0.
+  if (n_tiles > 0) {
+    dma_tile<D>(kbuf0, khead, kv_bytes, 0, wave, k_src, KS);
+    dma_tile<D>(vbuf0, vhead, kv_bytes, 0, wave, v_src, VS);
+    if (n_tiles > 1) dma_tile<D>(kbuf1, khead, kv_bytes, BC, wave, k_src, KS);
+  }
+  __syncthreads();
+  if (n_w > 0) {
+    qk_tile<T, D>(kbuf0, kr0, kr1, qf, sa);
+    mask_tile(0, sa);
+    l_run += fix_max(sa, pa, exp_tile<T>(sa, sl2, m_run, pa));
+    qk_tile<T, D>(kbuf1, kr0, kr1, qf, sb);
+  }
+  __syncthreads();
+  if (n_tiles > 2) dma_tile<D>(kbuf0, khead, kv_bytes, 2 * BC, wave, k_src, KS);
+  __syncthreads();
+
+  // Step i reads K tile i + 2 and V tile i while K tile i + 3 and V tile
+  // i + 1 load into the other buffers (last read in step i - 1; every wave
+  // passed the barrier that ended it).
+  auto issue_loads = [&](int i, uint8_t* kdst, uint8_t* vdst) {
+    if (i + 3 < n_tiles) dma_tile<D>(kdst, khead, kv_bytes, (i + 3) * BC, wave, k_src, KS);
+    if (i + 1 < n_tiles) dma_tile<D>(vdst, vhead, kv_bytes, (i + 1) * BC, wave, v_src, VS);
+  };
+  auto step = [&](int i, f32x16* se, const uint32_t* pc, f32x16* sn, uint32_t* pn,
+                  const uint8_t* kt, const uint8_t* vt) {
+    const bool live = i + 1 < n_w;  // is there a tile i + 1 for this wave?
+    if (live) mask_tile(i + 1, se);
+    float psum = fused_tile<T, D>(kt, kr0, kr1, qf, sn, vt, vr, pc, oacc, se, sl2, m_run, pn);
+    if (live) l_run += fix_max(se, pn, psum);
+  };
+
+  // Every wave runs n_tiles (loads, barrier) rounds and computes the first
+  // n_w of them; the barrier also waits for the wave's own loads.
+  for (int i = 0; i < n_w; i += 2) {
+    issue_loads(i, kbuf1, vbuf1);
+    step(i, sb, pa, sa, pb, kbuf0, vbuf0);
     __syncthreads();
-    if (j + 1 < n_w) {
-      issue_loads(j + 1, kbuf1, vbuf0);
-      step(j + 1, sb, sa, kbuf0, vbuf1);
+    if (i + 1 < n_w) {
+      issue_loads(i + 1, kbuf0, vbuf0);
+      step(i + 1, sa, pb, sb, pa, kbuf1, vbuf1);
       __syncthreads();
     }
   }
-  for (int j = n_w; j < n_tiles; ++j) {
-    if (j & 1)
-      issue_loads(j, kbuf1, vbuf0);
+  for (int i = n_w; i < n_tiles; ++i) {
+    if (i & 1)
+      issue_loads(i, kbuf0, vbuf0);
     else
-      issue_loads(j, kbuf0, vbuf1);
+      issue_loads(i, kbuf1, vbuf1);
     __syncthreads();
   }
 
