@@ -42,6 +42,8 @@
 //   and P stays below kSumLimit.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tile.h"
@@ -49,7 +51,6 @@
 namespace fa {
 namespace {
 
-constexpr int BR = 128;  // query rows per workgroup
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 // Largest per-lane sum of a tile's exponentials accepted without moving the
@@ -75,7 +76,7 @@ struct TileId {
 // round-robin (w % 8); when the key/value heads divide evenly over the XCDs,
 // every query tile of the query heads sharing one key/value head is kept on
 // one XCD so that head's K and V are reused from that XCD's L2.
-__device__ inline TileId tile_of(int w, const FwdArgs& a) {
+__device__ __forceinline__ TileId tile_of(int w, const FwdArgs& a) {
   TileId t;
   const int units = a.B * a.Hkv;
   if ((units & 7) == 0) {
@@ -102,7 +103,7 @@ __device__ inline TileId tile_of(int w, const FwdArgs& a) {
 // accumulator r of block kb holds key kb * 32 + acc_key(h, r) of this lane's
 // query row.
 template <typename T, int D>
-__device__ inline void qk_tile(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
+__device__ __forceinline__ void qk_tile(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
                                const typename T::vec8* qf, f32x16* s) {
   constexpr int RB = DmaTile<D>::RB;
   constexpr int KC = D / 16;
@@ -121,7 +122,7 @@ __device__ inline void qk_tile(const uint8_t* ks, uint32_t kb0, uint32_t kb1,
 // keys 16 ch + 8 h + 2t, +1 of this lane's row (the B operand of chunk ch of
 // O^T += V^T P^T); returns this lane's sum of the unrounded values.
 template <typename T>
-__device__ inline float exp_tile(const f32x16* s, float sl2, float m, uint32_t* pk) {
+__device__ __forceinline__ float exp_tile(const f32x16* s, float sl2, float m, uint32_t* pk) {
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -144,7 +145,7 @@ __device__ inline float exp_tile(const f32x16* s, float sl2, float m, uint32_t* 
 // share of the exponentials; scheduling fences keep that order. Returns this
 // lane's sum of the (unrounded) exponentials.
 template <typename T, int D>
-__device__ inline float fused_tile(const uint8_t* kt, uint32_t kr0, uint32_t kr1,
+__device__ __forceinline__ float fused_tile(const uint8_t* kt, uint32_t kr0, uint32_t kr1,
                                    const typename T::vec8* qf, f32x16* sn, const uint8_t* vt,
                                    uint32_t vr, const uint32_t* pc, f32x16* oacc,
                                    const f32x16* se, float sl2, float m, uint32_t* pn) {
@@ -209,25 +210,40 @@ __device__ inline float fused_tile(const uint8_t* kt, uint32_t kr0, uint32_t kr1
   return psum;
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// NW waves of 32 query rows per workgroup: 8 (256 rows, one workgroup per
+// CU, every staged K/V tile shared by 8 waves) when there are enough query
+// tiles to fill the GPU, else 4 (128 rows, two workgroups per CU).
+//
+// Key/value tiles go through two LDS buffers each, loaded directly from
+// global memory. Step i of the software pipeline reads K tile i + 2 and V
+// tile i while the loads of K tile i + 3 and V tile i + 1 are in flight.
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
+  constexpr int BR = 32 * NW;       // query rows per workgroup
   using V8 = typename T::vec8;
+  using DT = DmaTile<D, NW>;
   constexpr int KC = D / 16;  // k-chunks of the QK^T contraction
   constexpr int OD = D / 32;  // 32-wide output column blocks
+  constexpr int TB = DT::BYTES;
 
-  // Two K tile buffers, then two V tile buffers, filled by direct
-  // global -> LDS loads. K is staged one tile ahead of V: while the scores of
-  // tile j are exponentiated, the matrix cores already compute the scores of
-  // tile j + 1.
-  // Separate arrays (and a tile loop unrolled by two, so every access names
-  // its buffer statically) let the compiler see that a tile's operand reads
-  // never touch the buffers the in-flight loads are filling, so it does not
-  // make the reads wait for those loads.
-  constexpr int TB = DmaTile<D>::BYTES;
+  // One array per buffer: with the step loop unrolled by two every access
+  // names its buffer statically, so the compiler can see that a step's
+  // operand reads never touch the buffers the in-flight loads are filling
+  // and does not make the reads wait for those loads.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TB];
+  auto kslot = [&](int x) __attribute__((always_inline)) -> uint8_t* { return x ? kbuf1 : kbuf0; };
+  auto vslot = [&](int x) __attribute__((always_inline)) -> uint8_t* { return x ? vbuf1 : vbuf0; };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,23 +263,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int q0 = qt * BR + wave * 32;  // first query row of this wave
   const int qrow = q0 + c;             // the row this lane owns
 
-  const uint16_t* qptr = a.q + bh * Nq * D;
-  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * Nkv * D;
-  const uint32_t kv_bytes = (uint32_t)Nkv * D * 2u;
-  const uint16_t* const khead = a.k + kv_off;
-  const uint16_t* const vhead = a.v + kv_off;
-  const uint32_t k_src = k_dma_src<D>(wave, lane);
-  const uint32_t v_src = v_dma_src<D>(wave, lane);
-  const uint32_t kr0 = k_read_base<D>(h, c, 0);
-  const uint32_t kr1 = k_read_base<D>(h, c, 1);
-  const uint32_t vr = v_read_base<D>(h, c);
-
-  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8h .. +7].
-  V8 qf[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc)
-    qf[kc] = as_vec8<T>(qrow < Nq ? ld16(qptr + (size_t)qrow * D + kc * 16 + h * 8) : zero_u32x4());
-
   // Key tiles this workgroup stages, and the ones this wave computes (the
   // wave's rows may stop seeing keys earlier under the causal mask).
   const int kv_tiles = (Nkv + BC - 1) / BC;
@@ -275,6 +274,32 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   const int wave_last_key = CAUSAL ? min(Nq - 1, q0 + 31) + offset : Nkv - 1;
   const int n_w = (q0 >= Nq || wave_last_key < 0) ? 0 : min(n_tiles, wave_last_key / BC + 1);
 
+  const uint16_t* qptr = a.q + bh * Nq * D;
+  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * Nkv * D;
+  // Bytes of K / V the workgroup may read: loads of later tiles fill zeros
+  // without touching memory, so the pipeline may always issue its loads.
+  const uint32_t kv_bytes = (uint32_t)min(Nkv, n_tiles * BC) * D * 2u;
+  const uint16_t* const khead = a.k + kv_off;
+  const uint16_t* const vhead = a.v + kv_off;
+  const uint32_t k_src = k_dma_src<D, NW>(wave, lane);
+  const uint32_t v_src = v_dma_src<D, NW>(wave, lane);
+  const uint32_t kr0 = k_read_base<D>(h, c, 0);
+  const uint32_t kr1 = k_read_base<D>(h, c, 1);
+  const uint32_t vr = v_read_base<D>(h, c);
+  constexpr int KS = DT::K_STEP, VS = DT::V_STEP;
+  auto load_k = [&](int j, uint8_t* dst) __attribute__((always_inline)) {
+    dma_tile<D, NW>(dst, khead, kv_bytes, j * BC, wave, k_src, KS);
+  };
+  auto load_v = [&](int j, uint8_t* dst) __attribute__((always_inline)) {
+    dma_tile<D, NW>(dst, vhead, kv_bytes, j * BC, wave, v_src, VS);
+  };
+
+  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8h .. +7].
+  V8 qf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qf[kc] = as_vec8<T>(qrow < Nq ? ld16(qptr + (size_t)qrow * D + kc * 16 + h * 8) : zero_u32x4());
+
   f32x16 oacc[OD];
 #pragma unroll
   for (int od = 0; od < OD; ++od) oacc[od] = zero16();
@@ -282,11 +307,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   float l_run = 0.0f;       // this half-wave's share of the running sum
   const float sl2 = a.scale_log2;
 
-  constexpr int KS = DmaTile<D>::K_STEP, VS = DmaTile<D>::V_STEP;
-
   // Mask keys past the end and, when causal, keys after the row's limit, in
   // the scores s of tile j.
-  auto mask_tile = [&](int j, f32x16* s) {
+  auto mask_tile = [&](int j, f32x16* s) __attribute__((always_inline)) {
     const int key0 = j * BC;
     const bool need_mask = (key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset);
     if (need_mask) {
@@ -301,7 +324,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   // When the exponentials p of scores s (taken against m_run) summed to more
   // than kSumLimit in some row: move the maximum to the true running maximum,
   // rescale what U and l hold, and redo p. Returns the new sum.
-  auto fix_max = [&](const f32x16* s, uint32_t* p, float psum) {
+  auto fix_max = [&](const f32x16* s, uint32_t* p, float psum) __attribute__((always_inline)) {
     if (__builtin_expect(__any(!(psum <= kSumLimit)), 0)) {
       float mx = -INFINITY;
 #pragma unroll
@@ -325,18 +348,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   // Pipeline state entering step i: scores of tile i + 1 and the 16-bit P of
   // tile i (already counted in l). Step i computes the scores of tile i + 2,
   // U += P_i V_i and P of tile i + 1. The two score arrays and the two P
-  // arrays swap roles every step (the step loop is unrolled by two).
+  // arrays swap roles every step.
   f32x16 sa[2], sb[2];
   uint32_t pa[16], pb[16];
 
   // Prologue: K tiles 0 and 1 and V tile 0; scores and P of tile 0, scores
-  // of tile 1 (whatever K buffer 1 holds when there is no tile 1); then K
-  // tile 2 into the buffer of K tile 0.
-  if (n_tiles > 0) {
-    dma_tile<D>(kbuf0, khead, kv_bytes, 0, wave, k_src, KS);
-    dma_tile<D>(vbuf0, vhead, kv_bytes, 0, wave, v_src, VS);
-    if (n_tiles > 1) dma_tile<D>(kbuf1, khead, kv_bytes, BC, wave, k_src, KS);
-  }
+  // of tile 1; then K tile 2 into the buffer of K tile 0.
+  load_k(0, kbuf0);
+  load_k(1, kbuf1);
+  load_v(0, vbuf0);
   __syncthreads();
   if (n_w > 0) {
     qk_tile<T, D>(kbuf0, kr0, kr1, qf, sa);
@@ -345,18 +365,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
     qk_tile<T, D>(kbuf1, kr0, kr1, qf, sb);
   }
   __syncthreads();
-  if (n_tiles > 2) dma_tile<D>(kbuf0, khead, kv_bytes, 2 * BC, wave, k_src, KS);
-  __syncthreads();
+  load_k(2, kbuf0);
+  __syncthreads();  // K tile 2 is read by step 0
 
-  // Step i reads K tile i + 2 and V tile i while K tile i + 3 and V tile
-  // i + 1 load into the other buffers (last read in step i - 1; every wave
-  // passed the barrier that ended it).
-  auto issue_loads = [&](int i, uint8_t* kdst, uint8_t* vdst) {
-    if (i + 3 < n_tiles) dma_tile<D>(kdst, khead, kv_bytes, (i + 3) * BC, wave, k_src, KS);
-    if (i + 1 < n_tiles) dma_tile<D>(vdst, vhead, kv_bytes, (i + 1) * BC, wave, v_src, VS);
-  };
+  // Step i: loads of K tile i + 3 into buffer (i + 1) % 2 (last read for
+  // the scores computed in step i - 1) and V tile i + 1 into buffer
+  // (i + 1) % 2 (V tile i - 1, read in step i - 1); every wave passed the
+  // barrier ending step i - 1, so neither buffer is still being read.
   auto step = [&](int i, f32x16* se, const uint32_t* pc, f32x16* sn, uint32_t* pn,
-                  const uint8_t* kt, const uint8_t* vt) {
+                  const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     const bool live = i + 1 < n_w;  // is there a tile i + 1 for this wave?
     if (live) mask_tile(i + 1, se);
     float psum = fused_tile<T, D>(kt, kr0, kr1, qf, sn, vt, vr, pc, oacc, se, sl2, m_run, pn);
@@ -365,21 +382,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
 
   // Every wave runs n_tiles (loads, barrier) rounds and computes the first
   // n_w of them; the barrier also waits for the wave's own loads.
-  for (int i = 0; i < n_w; i += 2) {
-    issue_loads(i, kbuf1, vbuf1);
-    step(i, sb, pa, sa, pb, kbuf0, vbuf0);
-    __syncthreads();
-    if (i + 1 < n_w) {
-      issue_loads(i + 1, kbuf0, vbuf0);
-      step(i + 1, sa, pb, sb, pa, kbuf1, vbuf1);
-      __syncthreads();
-    }
+  for (int i0 = 0; i0 < n_w; i0 += 2) {
+    static_for<2>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
+      const int i = i0 + r;
+      if (i < n_w) {
+        load_k(i + 3, kslot(r ^ 1));
+        load_v(i + 1, vslot(r ^ 1));
+        if constexpr (r == 0)
+          step(i, sb, pa, sa, pb, kslot(0), vslot(0));
+        else
+          step(i, sa, pb, sb, pa, kslot(1), vslot(1));
+        __syncthreads();
+      }
+    });
   }
   for (int i = n_w; i < n_tiles; ++i) {
-    if (i & 1)
-      issue_loads(i, kbuf0, vbuf0);
-    else
-      issue_loads(i, kbuf1, vbuf1);
+    load_k(i + 3, kslot((i + 1) & 1));
+    load_v(i + 1, vslot((i + 1) & 1));
     __syncthreads();
   }
 
@@ -401,8 +421,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+template <typename T, int D, int NW>
+hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+  constexpr int BR = 32 * NW;
   FwdArgs a;
   a.q = static_cast<const uint16_t*>(t.q);
   a.k = static_cast<const uint16_t*>(t.k);
@@ -419,10 +440,17 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) 
   a.scale_log2 = p.scale * LOG2E;
   dim3 grid(a.n_qtiles * p.B * p.Hq);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
+}
+
+// 256-row workgroups when they alone fill the 256 CUs, else 128-row ones.
+template <typename T, int D>
+hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+  const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
+  return big_tiles >= 256 ? launch_nw<T, D, 8>(p, t, stream) : launch_nw<T, D, 4>(p, t, stream);
 }
 
 }  // namespace

@@ -132,28 +132,31 @@ __device__ inline void store_kv_tile(const KVTileRegs<D>& r, uint16_t* ks, uint1
 // i.e. 4 rows x 64 bytes per 256-byte block. A transposed read (16 lanes:
 // 4 consecutive rows x 32 bytes; 32 lanes: 4 rows x 64 bytes) stays inside
 // one such block and touches each bank once.
-template <int D>
+template <int D, int NW = 4>
 struct DmaTile {
-  static constexpr int RB = 2 * D;                  // bytes per key row
-  static constexpr int BYTES = BC * RB;             // bytes per tile
-  static constexpr int PER_WAVE = BYTES / 1024 / 4;  // 1 KiB DMA blocks per wave
-  static constexpr int K_STEP = 64;                 // source step between a wave's K blocks
-  static constexpr int V_STEP = 1024;               // source step between a wave's V blocks
+  static constexpr int RB = 2 * D;                   // bytes per key row
+  static constexpr int BYTES = BC * RB;              // bytes per tile
+  static constexpr int PER_WAVE = BYTES / 1024 / NW;  // 1 KiB DMA blocks per wave (NW waves)
+  static constexpr int K_STEP = 64;                  // source step between a wave's K blocks
+  static constexpr int V_STEP = 1024;                // source step between a wave's V blocks
+  static_assert((RB / 64) % PER_WAVE == 0, "a wave's K blocks share one 16-row group");
 };
 
 // Tile-relative source byte of lane l's chunk in the wave's first K block
 // (block i of the wave adds i * K_STEP).
-template <int D>
+template <int D, int NW>
 __device__ inline uint32_t k_dma_src(int wave, int l) {
-  using T = DmaTile<D>;
+  using T = DmaTile<D, NW>;
+  const int g = wave * T::PER_WAVE;  // first 1 KiB block: 16-row group m, 64-byte run G
+  const int m = g / (T::RB / 64), G = g % (T::RB / 64);
   const int u = l >> 2, slot = l & 3;
-  return (uint32_t)((16 * wave + u) * T::RB + (slot ^ (u >> 2)) * 16);
+  return (uint32_t)((16 * m + u) * T::RB + (4 * G + (slot ^ (u >> 2))) * 16);
 }
 
 // Same for V (block i adds i * V_STEP).
-template <int D>
+template <int D, int NW>
 __device__ inline uint32_t v_dma_src(int wave, int l) {
-  using T = DmaTile<D>;
+  using T = DmaTile<D, NW>;
   const int b = (T::PER_WAVE * wave) * 1024 + 16 * l;  // LDS byte of the wave's first block
   const int r4 = b / (4 * T::RB), rem = b % (4 * T::RB);
   const int q = 4 * (rem >> 8) + ((rem >> 4) & 3);
@@ -164,10 +167,10 @@ __device__ inline uint32_t v_dma_src(int wave, int l) {
 // Issue this wave's DMA loads of one K (or V) tile: `tile` is the tile's LDS
 // base, `head` the global base of the head's K (or V), `head_bytes` its size,
 // `key0` the tile's first key. Reads past the head's end fill zeros.
-template <int D>
+template <int D, int NW>
 __device__ inline void dma_tile(uint8_t* tile, const uint16_t* head, uint32_t head_bytes, int key0,
                                 int wave, uint32_t lane_src, int step) {
-  using T = DmaTile<D>;
+  using T = DmaTile<D, NW>;
 #pragma unroll
   for (int i = 0; i < T::PER_WAVE; ++i) {
     const uint32_t start = (uint32_t)key0 * T::RB + (uint32_t)(i * step);

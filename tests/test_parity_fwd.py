@@ -136,6 +136,8 @@ EDGE = [
     (3, 6, 3, 65, 129, 64, True),
     (1, 2, 1, 1, 1000, 128, True),     # decode, ragged split
     (2, 8, 2, 1, 64, 64, False),
+    (2, 64, 16, 1000, 1000, 128, True),  # 256-row workgroups, ragged last tile
+    (4, 32, 32, 700, 900, 64, False),    # 256-row workgroups, N_q < N_kv
 ]
 
 
