@@ -27,6 +27,7 @@ SOURCES = [
     "fa_fwd.hip",
     "fa_decode.hip",
     "fa_bwd.hip",
+    "fa_bwd_dq.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -11,26 +11,25 @@
 // (D_i equals sum_j P_ij dP_ij because O = P V.)
 //
 // Three stages on one stream:
-//   0  pre:   D_i for every query row; clear the float32 dQ accumulator.
-//   1  main:  one workgroup per 128-key block of one (b, kv head). K and V of
-//             the block stay in registers (and K row-major in LDS); the
-//             workgroup loops over the query heads of the group (GQA/MQA: dK,
-//             dV summed in registers, no atomics) and over the 64-row query
-//             tiles that can see the block (causal: only tiles at or below
-//             the diagonal). Q / dO tiles are double-buffered in LDS, the
-//             next one loading while the current one is used. Per tile:
+//   0  pre:   D_i for every query row (float32, in the workspace).
+//   1  dK/dV: one workgroup per 128-key block of one (b, kv head). K and V of
+//             the block stay in registers; the workgroup loops over the query
+//             heads of the group (GQA/MQA: dK, dV summed in registers, no
+//             atomics) and over the 64-row query tiles that can see the block
+//             (causal: only tiles at or below the diagonal). Q / dO tiles are
+//             double-buffered in LDS, the next one loading while the current
+//             one is used. Per tile:
 //               S = Q K^T and dP = dO V^T  (lane = key, 16 query rows / lane)
 //               P, dS in registers
 //               dV^T += dO^T P,  dK^T += Q^T dS   (accumulated in registers;
 //               the transposed operands come from transposed LDS reads)
-//               dS -> LDS as [query][key]; dQ += dS K for the 128 keys,
-//               added to the float32 accumulator with atomics
 //             and finally writes dK (times scale) and dV. When there are too
 //             few key blocks to fill the GPU (e.g. MQA), the query heads of a
 //             group are split over several workgroups, which write float32
 //             partial dK, dV to the workspace instead.
-//   2  dq:    dq = scale * accumulator, rounded to the input dtype; with a
-//             split head group, also dK = scale * sum of partials, dV = sum.
+//   2  dQ:    one workgroup per query tile recomputes P and dS over the key
+//             tiles and keeps dQ in registers (fa_bwd_dq.hip); with a split
+//             head group, also dK = scale * sum of partials, dV = sum.
 #include <math.h>
 
 #include "fa_device.h"
@@ -52,10 +51,8 @@ struct BwdArgs {
   const uint16_t* o;
   const float* lse;
   const uint16_t* dO;
-  uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;
   float* delta;
   float* dk_part;
   float* dv_part;
@@ -64,12 +61,11 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------- stage 0
-// D_i = sum_c dO_ic O_ic in float32; clear the dQ accumulator row.
+// D_i = sum_c dO_ic O_ic in float32.
 template <typename T, int D>
 __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ dq_acc, size_t rows) {
+                                                      float* __restrict__ delta, size_t rows) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int RPB = NTB / CPR;
   const int t = threadIdx.x;
@@ -84,10 +80,6 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
       acc = fmaf(T::to_float(a[i] & 0xffffu), T::to_float(g[i] & 0xffffu), acc);
       acc = fmaf(T::to_float(a[i] >> 16), T::to_float(g[i] >> 16), acc);
     }
-    f32x4 z;
-    z[0] = z[1] = z[2] = z[3] = 0.0f;
-    *reinterpret_cast<f32x4*>(dq_acc + row * D + ch * 8) = z;
-    *reinterpret_cast<f32x4*>(dq_acc + row * D + ch * 8 + 4) = z;
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
@@ -97,14 +89,11 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------- stage 1
 template <int D>
 struct BwdLds {
-  static constexpr int RS = D + 16;    // row stride of Q, dO, K tiles (32-byte pad)
-  static constexpr int SS = BKV + 16;  // row stride of dS [BQ][BKV]
+  static constexpr int RS = D + 16;    // row stride of Q, dO tiles (32-byte pad)
   static constexpr int TILE = BQ * RS;
-  static constexpr int Q_OFF = 0;                // [2][BQ][RS]
+  static constexpr int Q_OFF = 0;                  // [2][BQ][RS]
   static constexpr int DO_OFF = Q_OFF + 2 * TILE;  // [2][BQ][RS]
-  static constexpr int DS_OFF = DO_OFF + 2 * TILE; // [BQ][SS]
-  static constexpr int K_OFF = DS_OFF + BQ * SS;   // [BKV][RS]
-  static constexpr int ELEMS = K_OFF + BKV * RS;
+  static constexpr int ELEMS = DO_OFF + 2 * TILE;
 };
 
 // Q / dO tile of BQ rows (plus the rows' LSE and D) held in registers between
@@ -160,8 +149,11 @@ __device__ inline void store_q_tile(const QTileRegs<D>& r, uint16_t* qs, uint16_
   }
 }
 
+// Two workgroups per CU at d = 64; at d = 128 the stationary K, V and the
+// dK, dV accumulators alone take 192 of the 256 registers two waves per SIMD
+// would leave, so one.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTB, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs a) {
   using L = BwdLds<D>;
   using V8 = typename T::vec8;
   constexpr int KC = D / 16;
@@ -202,15 +194,6 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
     kf[kc] = as_vec8<T>(in ? ld16(kbase + (size_t)my_key * D + kc * 16 + h * 8) : zero_u32x4());
     vf[kc] = as_vec8<T>(in ? ld16(vbase + (size_t)my_key * D + kc * 16 + h * 8) : zero_u32x4());
   }
-  // The key block row-major in LDS: the B operand of dQ = dS K is read from
-  // it with transposed reads.
-  for (int id = tid; id < BKV * (D / 8); id += NTB) {
-    const int key = id / (D / 8), dc = id % (D / 8);
-    const bool in = kblk0 + key < Nkv;
-    *reinterpret_cast<u32x4*>(sm + L::K_OFF + key * L::RS + dc * 8) =
-        in ? ld16(kbase + (size_t)(kblk0 + key) * D + dc * 8) : zero_u32x4();
-  }
-
   f32x16 dk[OD], dv[OD];
 #pragma unroll
   for (int od = 0; od < OD; ++od) {
@@ -304,38 +287,6 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
         dk[od] = T::mfma(load_vt_operand<T, L::RS>(qs, h, c, ch * 16, od * 32), dsf, dk[od]);
       }
     }
-    // ---- dS to LDS as [query][key] (16-bit) for the dQ product.
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sm[L::DS_OFF + (qb * 32 + acc_key(h, r)) * L::SS + wave * 32 + c] = T::from_float(dp[qb][r]);
-    __syncthreads();
-
-    // ---- dQ[query][d] += sum over the block's 128 keys of dS K.
-    // Output tiles (query block qb, dim block od); D = 128: 8 tiles, 2 per
-    // wave; D = 64: 4 tiles, 1 per wave. Lane = dim column, so each atomic
-    // instruction touches 32 consecutive floats of two rows.
-    constexpr int TILES = 2 * OD;
-    constexpr int PER_WAVE = TILES / 4;
-#pragma unroll
-    for (int ti = 0; ti < PER_WAVE; ++ti) {
-      const int tile = wave * PER_WAVE + ti;
-      const int qb = tile / OD, od = tile % OD;
-      f32x16 acc = zero16();
-      const uint16_t* dsrow = sm + L::DS_OFF + (qb * 32 + c) * L::SS + h * 8;
-#pragma unroll
-      for (int ch = 0; ch < BKV / 16; ++ch) {
-        const V8 dsa = as_vec8<T>(*reinterpret_cast<const u32x4*>(dsrow + ch * 16));
-        acc = T::mfma(dsa, load_vt_operand<T, L::RS>(sm + L::K_OFF, h, c, ch * 16, od * 32), acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int query = qi0 + qb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (query < Nq) atomicAdd(a.dq_acc + (rowbase + query) * D + od * 32 + c, acc[r]);
-      }
-    }
-
     if (more)
       store_q_tile<D>(regs, sm + L::Q_OFF + (buf ^ 1) * L::TILE, sm + L::DO_OFF + (buf ^ 1) * L::TILE,
                       lse_s[buf ^ 1], del_s[buf ^ 1], tid);
@@ -385,22 +336,6 @@ __global__ __launch_bounds__(NTB) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- stage 2
-template <typename T>
-__global__ __launch_bounds__(NTB) void bwd_dq_kernel(const float* __restrict__ acc,
-                                                     uint16_t* __restrict__ dq, size_t n8,
-                                                     float scale) {
-  const size_t i = (size_t)blockIdx.x * NTB + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(acc + i * 8);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(acc + i * 8 + 4);
-  u32x4 out;
-  out[0] = pack2<T>(x0[0] * scale, x0[1] * scale);
-  out[1] = pack2<T>(x0[2] * scale, x0[3] * scale);
-  out[2] = pack2<T>(x1[0] * scale, x1[1] * scale);
-  out[3] = pack2<T>(x1[2] * scale, x1[3] * scale);
-  st16(dq + i * 8, out);
-}
-
 // dK = scale * sum of the partial sums, dV = sum, when the head group of a
 // key block was split across workgroups (fixed order: deterministic).
 template <typename T>
@@ -439,10 +374,8 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.o = static_cast<const uint16_t*>(t.o);
   a.lse = t.lse;
   a.dO = static_cast<const uint16_t*>(t.dO);
-  a.dq = static_cast<uint16_t*>(t.dq);
   a.dk = static_cast<uint16_t*>(t.dk);
   a.dv = static_cast<uint16_t*>(t.dv);
-  a.dq_acc = t.dq_acc;
   a.delta = t.delta;
   a.dk_part = t.dk_part;
   a.dv_part = t.dv_part;
@@ -467,7 +400,7 @@ hipError_t pre_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, dim3(NTB), 0, stream,
                      static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.delta,
-                     t.dq_acc, rows);
+                     rows);
   return hipGetLastError();
 }
 
@@ -485,14 +418,8 @@ hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
 
 template <typename T>
 hipError_t dq_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
-  const size_t n8 = (size_t)p.B * p.Hq * p.Nq * p.d / 8;
-  if (n8 > 0) {
-    dim3 grid((unsigned)((n8 + NTB - 1) / NTB));
-    hipLaunchKernelGGL((bwd_dq_kernel<T>), grid, dim3(NTB), 0, stream, t.dq_acc,
-                       static_cast<uint16_t*>(t.dq), n8, p.scale);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = launch_bwd_dq_rows(p, t, stream);
+  if (e != hipSuccess) return e;
   const int parts = bwd_group_split(p);
   const size_t n4 = (size_t)p.B * p.Hkv * p.Nkv * p.d / 4;
   if (parts > 1 && n4 > 0) {

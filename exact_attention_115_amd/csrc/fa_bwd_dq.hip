@@ -1,0 +1,255 @@
+// Backward, dQ (bf16 / fp16) on the gfx950 matrix cores.
+//
+// Method ([KB] "FlashAttention：为什么少搬数据，反而算得更快" §05: the forward
+// kept only O and the row statistic LSE, so each probability tile is rebuilt
+// on chip from it): for a tile of query rows, stream the key/value tiles the
+// rows may see (as in the forward, [BLOG] §五 outer loop over query tiles,
+// inner loop over key/value tiles) and per tile recompute
+//   S = scale Q K^T,  P = exp(S - LSE),  dP = dO V^T,  dS = P (dP - D),
+// with D_i = sum_c dO_ic O_ic from the first backward stage, then add
+//   dQ += scale dS K.
+// dQ stays in registers for the whole key range and is written once, in the
+// input dtype: no atomics, no float32 accumulator in memory.
+//
+// gfx950 mapping (as the forward kernel): one query row per lane; S^T = K Q^T
+// and dP^T = V dO^T on v_mfma_f32_32x32x16 with Q and dO held as B operands
+// in registers and K, V rows read from LDS; the rows' LSE and D are lane
+// constants; dS^T is rounded to 16 bits in registers and is directly the B
+// operand of dQ^T += K^T dS^T, whose A operand comes from transposed LDS
+// reads of the same K tile. K and V tiles are double-buffered in LDS and
+// filled by direct global -> LDS loads one tile ahead.
+#include <math.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+#include "fa_tile.h"
+
+namespace fa {
+namespace {
+
+constexpr float LOG2E = 1.44269504088896340736f;
+
+struct DqArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dO;
+  const float* lse;
+  const float* delta;
+  uint16_t* dq;
+  int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
+  float scale, scale_log2;
+};
+
+// X^T from the K-layout tile at xs (xs: K or V), as in the forward's scores:
+// accumulator r of block kb holds key kb * 32 + acc_key(h, r) of this lane's
+// query row, for the B operand xf (Q or dO of the row).
+template <typename T, int D>
+__device__ __forceinline__ void row_products(const uint8_t* xs, uint32_t kb0, uint32_t kb1,
+                                             const typename T::vec8* xf, f32x16* s) {
+  constexpr int RB = DmaTile<D>::RB;
+  constexpr int KC = D / 16;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    s[kb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint8_t* p = xs + ((kc & 1) ? kb1 : kb0) + kb * 32 * RB + (kc >> 1) * 1024;
+      s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), xf[kc], s[kb]);
+    }
+  }
+}
+
+// NW waves of 32 query rows per workgroup (8 when the grid fills the GPU,
+// else 4), as in the forward.
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
+  constexpr int BR = 32 * NW;
+  using V8 = typename T::vec8;
+  using DT = DmaTile<D, NW>;
+  constexpr int KC = D / 16;
+  constexpr int OD = D / 32;
+  constexpr int TB = DT::BYTES;
+
+  // K and V tiles, both in the K layout (rows read for the products with Q
+  // and dO, K also read transposed for dQ); one array per buffer so every
+  // access names its buffer statically (the step loop is unrolled by two).
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[TB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int c = lane & 31;
+
+  const TileId id = tile_of(blockIdx.x, a.B, a.Hq, a.Hkv, a.G, a.n_qtiles);
+  const int qt = id.qt, b = id.b, hq = id.hq;
+  const int hkv = hq / a.G;
+  const int Nq = a.Nq, Nkv = a.Nkv;
+  const int offset = Nkv - Nq;
+  const size_t bh = (size_t)b * a.Hq + hq;
+  const int q0 = qt * BR + wave * 32;
+  const int qrow = q0 + c;
+  const bool has_row = qrow < Nq;
+
+  const int kv_tiles = (Nkv + BC - 1) / BC;
+  int n_tiles = kv_tiles;
+  if (CAUSAL) {
+    const int last_key = min(Nq, (qt + 1) * BR) - 1 + offset;
+    n_tiles = last_key < 0 ? 0 : min(kv_tiles, last_key / BC + 1);
+  }
+  const int wave_last_key = CAUSAL ? min(Nq - 1, q0 + 31) + offset : Nkv - 1;
+  const int n_w = (q0 >= Nq || wave_last_key < 0) ? 0 : min(n_tiles, wave_last_key / BC + 1);
+
+  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * Nkv * D;
+  const uint32_t kv_bytes = (uint32_t)min(Nkv, n_tiles * BC) * D * 2u;
+  const uint16_t* const khead = a.k + kv_off;
+  const uint16_t* const vhead = a.v + kv_off;
+  const uint32_t src = k_dma_src<D, NW>(wave, lane);
+  const uint32_t kr0 = k_read_base<D>(h, c, 0);
+  const uint32_t kr1 = k_read_base<D>(h, c, 1);
+  const uint32_t kt0 = kt_read_base<D>(h, c, 0);
+  const uint32_t kt1 = kt_read_base<D>(h, c, 1);
+  auto load_kv = [&](int j, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
+    dma_tile<D, NW>(kd, khead, kv_bytes, j * BC, wave, src, DT::K_STEP);
+    dma_tile<D, NW>(vd, vhead, kv_bytes, j * BC, wave, src, DT::K_STEP);
+  };
+
+  // Q and dO of this lane's row as B operands; its LSE (log2 units; +inf for
+  // a row that saw no key, so P = 0) and D.
+  const uint16_t* qp = a.q + (bh * Nq + qrow) * D;
+  const uint16_t* gp = a.dO + (bh * Nq + qrow) * D;
+  V8 qf[KC], gf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qf[kc] = as_vec8<T>(has_row ? ld16(qp + kc * 16 + h * 8) : zero_u32x4());
+    gf[kc] = as_vec8<T>(has_row ? ld16(gp + kc * 16 + h * 8) : zero_u32x4());
+  }
+  float lse2 = INFINITY, drow = 0.0f;
+  if (has_row) {
+    const float l = a.lse[bh * Nq + qrow];
+    if (l != -INFINITY) lse2 = l * LOG2E;
+    drow = a.delta[bh * Nq + qrow];
+  }
+  const float sl2 = a.scale_log2;
+
+  f32x16 acc[OD];
+#pragma unroll
+  for (int od = 0; od < OD; ++od) acc[od] = zero16();
+
+  auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    f32x16 s[2], dp[2];
+    row_products<T, D>(kt, kr0, kr1, qf, s);
+    row_products<T, D>(vt, kr0, kr1, gf, dp);
+    const int key0 = j * BC;
+    if ((key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset)) {
+      const int lim = CAUSAL ? min(Nkv - 1, qrow + offset) : Nkv - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
+    }
+    // dS = P (dP - D), rounded to 16 bits: ds[4 ch + t] holds the keys
+    // 16 ch + 8 h + 2t, +1 (the B operand of chunk ch of dQ^T += K^T dS^T).
+    uint32_t ds[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kb = i >> 3, r = 2 * (i & 7);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -lse2));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -lse2));
+      ds[i] = pack2<T>(p0 * (dp[kb][r] - drow), p1 * (dp[kb][r + 1] - drow));
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      u32x4 w;
+      w[0] = ds[4 * ch + 0];
+      w[1] = ds[4 * ch + 1];
+      w[2] = ds[4 * ch + 2];
+      w[3] = ds[4 * ch + 3];
+      const V8 bf = as_vec8<T>(w);
+#pragma unroll
+      for (int od = 0; od < OD; ++od)
+        acc[od] = T::mfma(load_kt_dma<T, D>(kt, kt0, kt1, ch, od), bf, acc[od]);
+    }
+  };
+
+  // Tile j is computed from buffers j % 2 while tile j + 1 loads into the
+  // others (last read during tile j - 1; every wave passed the barrier that
+  // ended it). Every wave runs n_tiles rounds and computes the first n_w.
+  load_kv(0, kbuf0, vbuf0);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j += 2) {
+    load_kv(j + 1, kbuf1, vbuf1);
+    if (j < n_w) compute(j, kbuf0, vbuf0);
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      load_kv(j + 2, kbuf0, vbuf0);
+      if (j + 1 < n_w) compute(j + 1, kbuf1, vbuf1);
+      __syncthreads();
+    }
+  }
+
+  // dQ = scale * sum over key tiles of dS K (lane = query row, accumulator
+  // rows = dims).
+  if (has_row) {
+    uint16_t* row = a.dq + (bh * Nq + qrow) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int od = 0; od < OD; ++od)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 out;
+        out[0] = pack2<T>(acc[od][4 * g + 0] * sc, acc[od][4 * g + 1] * sc);
+        out[1] = pack2<T>(acc[od][4 * g + 2] * sc, acc[od][4 * g + 3] * sc);
+        *reinterpret_cast<u32x2*>(row + od * 32 + g * 8 + h * 4) = out;
+      }
+  }
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
+  DqArgs a;
+  a.q = static_cast<const uint16_t*>(t.q);
+  a.k = static_cast<const uint16_t*>(t.k);
+  a.v = static_cast<const uint16_t*>(t.v);
+  a.dO = static_cast<const uint16_t*>(t.dO);
+  a.lse = t.lse;
+  a.delta = t.delta;
+  a.dq = static_cast<uint16_t*>(t.dq);
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
+  a.Nq = p.Nq;
+  a.Nkv = p.Nkv;
+  a.n_qtiles = (p.Nq + 32 * NW - 1) / (32 * NW);
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * LOG2E;
+  dim3 grid((unsigned)(a.n_qtiles * p.B * p.Hq));
+  if (p.causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, NW>), grid, dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, NW>), grid, dim3(64 * NW), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
+  const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
+  return big_tiles >= 256 ? launch_nw<T, D, 8>(p, t, stream) : launch_nw<T, D, 4>(p, t, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_rows(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
+  if ((size_t)p.B * p.Hq * p.Nq == 0) return hipSuccess;
+  if (p.dt == FA_BF16)
+    return p.d == 64 ? launch_typed<BF16, 64>(p, t, stream) : launch_typed<BF16, 128>(p, t, stream);
+  return p.d == 64 ? launch_typed<F16, 64>(p, t, stream) : launch_typed<F16, 128>(p, t, stream);
+}
+
+}  // namespace fa

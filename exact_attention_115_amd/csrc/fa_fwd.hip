@@ -67,37 +67,6 @@ struct FwdArgs {
   float scale_log2;
 };
 
-struct TileId {
-  int qt, b, hq;
-};
-
-// Workgroup w -> (query tile, batch, query head). Heaviest (last, under the
-// causal mask) query tiles go first. Workgroups are handed to the 8 XCDs
-// round-robin (w % 8); when the key/value heads divide evenly over the XCDs,
-// every query tile of the query heads sharing one key/value head is kept on
-// one XCD so that head's K and V are reused from that XCD's L2.
-__device__ __forceinline__ TileId tile_of(int w, const FwdArgs& a) {
-  TileId t;
-  const int units = a.B * a.Hkv;
-  if ((units & 7) == 0) {
-    const int xcd = w & 7;
-    const int j = w >> 3;
-    const int per_level = (units >> 3) * a.G;  // workgroups per tile row, per XCD
-    t.qt = a.n_qtiles - 1 - j / per_level;
-    const int rem = j % per_level;
-    const int u = xcd + 8 * (rem / a.G);
-    t.b = u / a.Hkv;
-    t.hq = (u % a.Hkv) * a.G + rem % a.G;
-  } else {
-    const int n_bh = a.B * a.Hq;
-    t.qt = a.n_qtiles - 1 - w / n_bh;
-    const int bh = w % n_bh;
-    t.b = bh / a.Hq;
-    t.hq = bh % a.Hq;
-  }
-  return t;
-}
-
 // S^T = K Q^T for the 64 keys of the K tile at ks (DMA layout; kb0, kb1:
 // this lane's k_read_base for even and odd kc): two 32-key blocks,
 // accumulator r of block kb holds key kb * 32 + acc_key(h, r) of this lane's
@@ -251,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   const int h = lane >> 5;
   const int c = lane & 31;
 
-  const TileId id = tile_of(blockIdx.x, a);
+  const TileId id = tile_of(blockIdx.x, a.B, a.Hq, a.Hkv, a.G, a.n_qtiles);
   const int qt = id.qt;
   const int b = id.b;
   const int hq = id.hq;

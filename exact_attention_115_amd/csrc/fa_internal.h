@@ -37,8 +37,7 @@ struct BwdPtrs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;     // [B, Hq, Nq, d] float32, in the workspace
-  float* delta;      // [B, Hq, Nq]    float32, in the workspace
+  float* delta;      // [B, Hq, Nq] float32, in the workspace
   float* dk_part;    // [gsplit, B, Hkv, Nkv, d] float32 partial sums, or NULL
   float* dv_part;    //   (present only when the head group is split)
 };
@@ -65,5 +64,7 @@ hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream)
 hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 hipError_t launch_bwd_dq(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+// The query-stationary dQ kernel (part of launch_bwd_dq).
+hipError_t launch_bwd_dq_rows(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 
 }  // namespace fa

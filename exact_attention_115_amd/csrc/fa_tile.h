@@ -247,4 +247,62 @@ __device__ inline typename T::vec8 load_vt_dma(const uint8_t* vt, uint32_t vb, i
   return __builtin_bit_cast(typename T::vec8, x);
 }
 
+// Transposed reads from a K-layout tile (the layout supports both 16-byte
+// row reads and transposed reads without bank conflicts: a transposed read
+// touches 4 consecutive rows of one 16-row group, which sit in distinct
+// 64-byte slots). The A operand X^T[dim0 + c][key0 + 8h .. +7] with
+// dim0 = 32 od, key0 = 16 ch: lane (h, c), j = c % 16, reads row
+// 16 ch + 8h + 4s + j / 4 at element column 32 od + 16 (c / 16) + 4 (j % 4),
+// i.e. byte kt_read_base(h, c, s) + ch * 16 RB + od * 1024.
+template <int D>
+__device__ inline uint32_t kt_read_base(int h, int c, int s) {
+  const int j = c & 15;
+  const int q3 = 2 * (c >> 4) + ((j >> 1) & 1);  // chunk within the 64-byte run
+  return (uint32_t)((8 * h + 4 * s + (j >> 2)) * 64 + ((q3 ^ (2 * h + s)) << 4) + 8 * (j & 1));
+}
+
+template <typename T, int D>
+__device__ inline typename T::vec8 load_kt_dma(const uint8_t* kt, uint32_t b0, uint32_t b1, int ch,
+                                               int od) {
+  constexpr int RB = DmaTile<D>::RB;
+  const s16x4 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(kt + b0 + ch * 16 * RB + od * 1024));
+  const s16x4 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(kt + b1 + ch * 16 * RB + od * 1024));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 x;
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+  x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+  return __builtin_bit_cast(typename T::vec8, x);
+}
+
+struct TileId {
+  int qt, b, hq;
+};
+
+// Workgroup w -> (query tile, batch, query head). Heaviest (last, under the
+// causal mask) query tiles go first. Workgroups are handed to the 8 XCDs
+// round-robin (w % 8); when the key/value heads divide evenly over the XCDs,
+// every query tile of the query heads sharing one key/value head is kept on
+// one XCD so that head's K and V are reused from that XCD's L2.
+__device__ __forceinline__ TileId tile_of(int w, int B, int Hq, int Hkv, int G, int n_qtiles) {
+  TileId t;
+  const int units = B * Hkv;
+  if ((units & 7) == 0) {
+    const int xcd = w & 7;
+    const int j = w >> 3;
+    const int per_level = (units >> 3) * G;  // workgroups per tile row, per XCD
+    t.qt = n_qtiles - 1 - j / per_level;
+    const int rem = j % per_level;
+    const int u = xcd + 8 * (rem / G);
+    t.b = u / Hkv;
+    t.hq = (u % Hkv) * G + rem % G;
+  } else {
+    const int n_bh = B * Hq;
+    t.qt = n_qtiles - 1 - w / n_bh;
+    const int bh = w % n_bh;
+    t.b = bh / Hq;
+    t.hq = bh % Hq;
+  }
+  return t;
+}
+
 }  // namespace fa

@@ -53,14 +53,14 @@ def test_workspace_sizes():
     assert ws > 0 and ws % 256 == 0
     rows = ws // (129 * 4)
     assert rows % (16 * 32) == 0
-    # Backward: float32 dQ accumulator + float32 row terms, linear in N.
+    # Backward: the float32 row terms D, linear in N.
     for B, Hq, Hkv, N, d in [(1, 32, 32, 4096, 128), (2, 16, 16, 1024, 64), (4, 32, 8, 2048, 128)]:
-        want = _align(B * Hq * N * d * 4) + _align(B * Hq * N * 4)
+        want = _align(B * Hq * N * 4)
         assert lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) == want
     # MQA with few key blocks: the head group is split over s workgroups, which
     # adds float32 partial dK and dV planes (s of each), s a divisor of G.
     B, Hq, Hkv, N, d = 4, 32, 1, 2048, 128
-    base = _align(B * Hq * N * d * 4) + _align(B * Hq * N * 4)
+    base = _align(B * Hq * N * 4)
     extra = lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) - base
     plane = B * Hkv * N * d * 4
     assert extra > 0 and extra % (2 * plane) == 0
@@ -135,7 +135,8 @@ def test_bwd_rejects_bad_arguments():
     assert bwd(do=None) == -1
     assert bwd(dk=None) == -1
     assert bwd(ws=None) == -1
-    assert bwd(ws_bytes=1024) == -5
+    need = fa.load().fa_bwd_workspace_size(1, 2, 2, 64, 64, 64, fa.FA_BF16)
+    assert need > 0 and bwd(ws_bytes=need - 1) == -5
     assert bwd(ws=P(10, 64)) == -4
     assert bwd(dq=P(7, 2)) == -4
     assert bwd(Hq=4, Hkv=3) == -2
