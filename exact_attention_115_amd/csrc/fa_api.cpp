@@ -161,12 +161,13 @@ BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, 
   const size_t del = align_up(rows * sizeof(float), 256);
   char* base = static_cast<char*>(ws);
   t.delta = reinterpret_cast<float*>(base);
+  t.lse2 = base ? reinterpret_cast<float*>(base + del) : nullptr;
   t.dk_part = t.dv_part = nullptr;
   const int gs = bwd_group_split(p);
   if (gs > 1 && base) {
     const size_t part = align_up((size_t)gs * p.B * p.Hkv * p.Nkv * p.d * sizeof(float), 256);
-    t.dk_part = reinterpret_cast<float*>(base + del);
-    t.dv_part = reinterpret_cast<float*>(base + del + part);
+    t.dk_part = reinterpret_cast<float*>(base + 2 * del);
+    t.dv_part = reinterpret_cast<float*>(base + 2 * del + part);
   }
   return t;
 }
@@ -222,7 +223,7 @@ size_t bwd_workspace_bytes(const Problem& p) {
   const size_t rows = (size_t)p.B * p.Hq * p.Nq;
   const size_t kv = (size_t)p.B * p.Hkv * p.Nkv * p.d;
   if (rows == 0 && kv == 0) return 0;
-  size_t bytes = align_up(rows * sizeof(float), 256);
+  size_t bytes = 2 * align_up(rows * sizeof(float), 256);
   const int gs = bwd_group_split(p);
   if (gs > 1) bytes += 2 * align_up((size_t)gs * kv * sizeof(float), 256);
   return bytes;

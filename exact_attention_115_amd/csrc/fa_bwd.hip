@@ -32,6 +32,8 @@
 //             head group, also dK = scale * sum of partials, dV = sum.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 #include "fa_tile.h"
@@ -53,6 +55,7 @@ struct BwdArgs {
   const uint16_t* dO;
   uint16_t* dk;
   uint16_t* dv;
+  const float* lse2;   // LSE * log2(e) per query row (+inf: row saw no key)
   float* delta;
   float* dk_part;
   float* dv_part;
@@ -61,11 +64,14 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------- stage 0
-// D_i = sum_c dO_ic O_ic in float32.
+// D_i = sum_c dO_ic O_ic in float32, and LSE2_i = LSE_i log2(e) (+inf for a
+// row that saw no key, so that exp2(S scale log2(e) - LSE2) = P is 0).
 template <typename T, int D>
 __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta, size_t rows) {
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ delta,
+                                                      float* __restrict__ lse2, size_t rows) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int RPB = NTB / CPR;
   const int t = threadIdx.x;
@@ -83,95 +89,214 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && ch == 0) delta[row] = acc;
+  if (row < rows && ch == 0) {
+    delta[row] = acc;
+    const float l = lse[row];
+    lse2[row] = l == -INFINITY ? INFINITY : l * LOG2E;
+  }
 }
 
 // ---------------------------------------------------------------- stage 1
-template <int D>
-struct BwdLds {
-  static constexpr int RS = D + 16;    // row stride of Q, dO tiles (32-byte pad)
-  static constexpr int TILE = BQ * RS;
-  static constexpr int Q_OFF = 0;                  // [2][BQ][RS]
-  static constexpr int DO_OFF = Q_OFF + 2 * TILE;  // [2][BQ][RS]
-  static constexpr int ELEMS = DO_OFF + 2 * TILE;
-};
-
-// Q / dO tile of BQ rows (plus the rows' LSE and D) held in registers between
-// the global loads and the LDS write, so the loads of the next tile overlap
-// the work on the current one.
-template <int D>
-struct QTileRegs {
-  static constexpr int CH = (BQ * D / 8) / NTB;  // 16-byte chunks per thread, per tensor
-  u32x4 q[CH];
-  u32x4 g[CH];
-  float lse2, delta;
-};
-
-template <int D>
-__device__ inline void load_q_tile(QTileRegs<D>& r, const uint16_t* __restrict__ qh,
-                                   const uint16_t* __restrict__ doh, const float* __restrict__ lse,
-                                   const float* __restrict__ delta, int qi0, int Nq, int tid) {
-#pragma unroll
-  for (int i = 0; i < QTileRegs<D>::CH; ++i) {
-    const int id = tid + NTB * i;
-    const int row = id / (D / 8), dc = id % (D / 8);
-    const bool in = qi0 + row < Nq;
-    const size_t off = (size_t)(qi0 + row) * D + dc * 8;
-    r.q[i] = in ? ld16(qh + off) : zero_u32x4();
-    r.g[i] = in ? ld16(doh + off) : zero_u32x4();
+// One step of the dK/dV pipeline for query tile i, as a single interleaved
+// instruction stream of three independent parts:
+//   * scores and dP of tile i + 1: sn = Q' K^T, dpn = dO' V^T (rows of the
+//     next Q / dO tiles read from LDS; K, V stationary B operands)
+//   * dV^T += dO^T P and dK^T += Q^T dS of tile i - 1 (PREV; transposed LDS
+//     reads of that tile's Q / dO, its P and dS already rounded in pp, dsp)
+//   * P = exp2(S scale_log2 - LSE2) and dS = P (dP - D) of tile i, rounded
+//     to 16 bits into pc, dsc (lse / dl: the tile's LSE2 and D rows in LDS)
+// Matrix-core products alternate between row and transposed products; LDS
+// operands are read two products of their kind ahead; scheduling fences keep
+// the order. Element pair e of a lane is keys' query rows 32 (e / 8) +
+// acc_key(h, 2 (e % 8)), +1 (consecutive), and pc[4 ch + t] / dsc[4 ch + t]
+// hold query rows 16 ch + 8 h + 2t, +1: the B operands of chunk ch.
+template <typename T, int D, bool PREV>
+__device__ __forceinline__ void dkdv_step(
+    const uint8_t* qn, const uint8_t* gn, const uint8_t* qp, const uint8_t* gp, uint32_t kr0,
+    uint32_t kr1, uint32_t kt0, uint32_t kt1, const typename T::vec8* kf, const typename T::vec8* vf,
+    f32x16* sn, f32x16* dpn, f32x16* dk, f32x16* dv, const uint32_t* pp, const uint32_t* dsp,
+    const f32x16* s, const f32x16* dpc, const float* lse, const float* dl, int h, float sl2,
+    uint32_t* pc, uint32_t* dsc) {
+  using V8 = typename T::vec8;
+  constexpr int RB = DmaTile<D>::RB;
+  constexpr int KC = D / 16;
+  constexpr int OD = D / 32;
+  constexpr int NR = 4 * KC;  // row products: x = r % 2 (S / dP), qb = (r / 2) % 2, kc = r / 4
+  constexpr int NT = 8 * OD;  // transposed products: y = t % 2 (dV / dK), ch = (t / 2) / OD, od = (t / 2) % OD
+  constexpr int NM = NR + NT;
+  static_assert(64 % NM == 0, "whole parts per product");
+  auto rfrag = [&](int r) {
+    const int x = r & 1, qb = (r >> 1) & 1, kc = r >> 2;
+    return *reinterpret_cast<const u32x4*>((x ? gn : qn) + ((kc & 1) ? kr1 : kr0) + qb * 32 * RB +
+                                           (kc >> 1) * 1024);
+  };
+  auto tfrag = [&](int t) {
+    const int y = t & 1, ch = (t >> 1) / OD, od = (t >> 1) % OD;
+    return load_kt_dma<T, D>(y ? qp : gp, kt0, kt1, ch, od);
+  };
+  sn[0] = zero16();
+  sn[1] = zero16();
+  dpn[0] = zero16();
+  dpn[1] = zero16();
+  u32x4 rf[NR];
+  V8 tf[NT];
+  rf[0] = rfrag(0);
+  rf[1] = rfrag(1);
+  if constexpr (PREV) {
+    tf[0] = tfrag(0);
+    tf[1] = tfrag(1);
   }
-  if (tid < BQ) {
-    const int row = qi0 + tid;
-    r.lse2 = INFINITY;  // rows past the end, and rows that saw no key: P = 0
-    r.delta = 0.0f;
-    if (row < Nq) {
-      const float l = lse[row];
-      if (l != -INFINITY) r.lse2 = l * LOG2E;
-      r.delta = delta[row];
+  float e0 = 0.0f, e1 = 0.0f;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int i = m >> 1;
+    if ((m & 1) == 0) {
+      if (i + 2 < NR) rf[i + 2] = rfrag(i + 2);
+      const int x = i & 1, qb = (i >> 1) & 1, kc = i >> 2;
+      if (x)
+        dpn[qb] = T::mfma(as_vec8<T>(rf[i]), vf[kc], dpn[qb]);
+      else
+        sn[qb] = T::mfma(as_vec8<T>(rf[i]), kf[kc], sn[qb]);
+    } else if constexpr (PREV) {
+      if (i + 2 < NT) tf[i + 2] = tfrag(i + 2);
+      const int y = i & 1, ch = (i >> 1) / OD, od = (i >> 1) % OD;
+      const uint32_t* w4 = (y ? dsp : pp) + 4 * ch;
+      u32x4 w;
+      w[0] = w4[0];
+      w[1] = w4[1];
+      w[2] = w4[2];
+      w[3] = w4[3];
+      if (y)
+        dk[od] = T::mfma(tf[i], as_vec8<T>(w), dk[od]);
+      else
+        dv[od] = T::mfma(tf[i], as_vec8<T>(w), dv[od]);
+    }
+    // Tile i's P and dS: the 16 pairs in four parts each (fma + exp, the
+    // rounding of P, the dS factors, the rounding of dS), spread evenly
+    // over the NM products.
+    constexpr int PARTS = 64 / NM;  // parts per product: 1 (d = 128) or 2 (d = 64)
+#pragma unroll
+    for (int u = 0; u < PARTS; ++u) {
+      const int pidx = m * PARTS + u;
+      const int e = pidx >> 2, part = pidx & 3;
+      const int kb = e >> 3, r = 2 * (e & 7);
+      const int q = kb * 32 + acc_key(h, r);
+      if (part == 0) {
+        const float2 l2 = *reinterpret_cast<const float2*>(lse + q);
+        e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -l2.x));
+        e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -l2.y));
+      } else if (part == 1) {
+        pc[e] = pack2<T>(e0, e1);
+      } else if (part == 2) {
+        const float2 d2 = *reinterpret_cast<const float2*>(dl + q);
+        e0 = e0 * (dpc[kb][r] - d2.x);
+        e1 = e1 * (dpc[kb][r + 1] - d2.y);
+      } else {
+        dsc[e] = pack2<T>(e0, e1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS of one tile (the pipeline's last).
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_tail(const uint8_t* qp, const uint8_t* gp, uint32_t kt0,
+                                          uint32_t kt1, f32x16* dk, f32x16* dv, const uint32_t* pp,
+                                          const uint32_t* dsp) {
+  using V8 = typename T::vec8;
+  constexpr int OD = D / 32;
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    u32x4 wp, ws;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      wp[t] = pp[4 * ch + t];
+      ws[t] = dsp[4 * ch + t];
+    }
+#pragma unroll
+    for (int od = 0; od < OD; ++od) {
+      dv[od] = T::mfma(load_kt_dma<T, D>(gp, kt0, kt1, ch, od), as_vec8<T>(wp), dv[od]);
+      dk[od] = T::mfma(load_kt_dma<T, D>(qp, kt0, kt1, ch, od), as_vec8<T>(ws), dk[od]);
     }
   }
 }
 
-template <int D>
-__device__ inline void store_q_tile(const QTileRegs<D>& r, uint16_t* qs, uint16_t* gs,
-                                    float* lse_s, float* del_s, int tid) {
-  using L = BwdLds<D>;
+// Rows of a Q-like tile: S[query][key] (accumulator r of block qb holds
+// query qb * 32 + acc_key(h, r), lane column = this wave's key c) from the
+// K-layout tile xs and the stationary B operand xf.
+template <typename T, int D>
+__device__ __forceinline__ void tile_rows(const uint8_t* xs, uint32_t kb0, uint32_t kb1,
+                                          const typename T::vec8* xf, f32x16* s) {
+  constexpr int RB = DmaTile<D>::RB;
+  constexpr int KC = D / 16;
 #pragma unroll
-  for (int i = 0; i < QTileRegs<D>::CH; ++i) {
-    const int id = tid + NTB * i;
-    const int row = id / (D / 8), dc = id % (D / 8);
-    *reinterpret_cast<u32x4*>(qs + row * L::RS + dc * 8) = r.q[i];
-    *reinterpret_cast<u32x4*>(gs + row * L::RS + dc * 8) = r.g[i];
-  }
-  if (tid < BQ) {
-    lse_s[tid] = r.lse2;
-    del_s[tid] = r.delta;
+  for (int qb = 0; qb < 2; ++qb) {
+    s[qb] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const uint8_t* p = xs + ((kc & 1) ? kb1 : kb0) + qb * 32 * RB + (kc >> 1) * 1024;
+      s[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), xf[kc], s[qb]);
+    }
   }
 }
 
-// Two workgroups per CU at d = 64; at d = 128 the stationary K, V and the
-// dK, dV accumulators alone take 192 of the 256 registers two waves per SIMD
-// would leave, so one.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// One workgroup of 4 waves per 128-key block (32 keys per wave) of one
+// (b, kv head) and one share of the head group. Q / dO tiles of BQ = 64 rows
+// (and their LSE2, D rows) go through a ring of 4 LDS slots filled by direct
+// global -> LDS loads two tiles ahead; step i reads tile i + 1 (rows), tile
+// i (LSE2, D) and tile i - 1 (transposed). One wave per SIMD: the stationary
+// K, V, the dK, dV accumulators and two tiles of scores and P need more than
+// the 256 registers two waves per SIMD would leave.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NTB, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs a) {
-  using L = BwdLds<D>;
+__global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using V8 = typename T::vec8;
+  using DT = DmaTile<D, 4>;
   constexpr int KC = D / 16;
   constexpr int OD = D / 32;
+  constexpr int TB = DT::BYTES;
+  static_assert(BQ == BC, "query tiles use the key-tile layout");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sm[L::ELEMS];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float del_s[2][BQ];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs3[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t gs0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t gs1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t gs2[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t gs3[TB];
+  __shared__ __attribute__((aligned(256))) float ls0[BQ], ls1[BQ], ls2[BQ], ls3[BQ];
+  __shared__ __attribute__((aligned(256))) float ds0[BQ], ds1[BQ], ds2[BQ], ds3[BQ];
+  auto qslot = [&](int x) __attribute__((always_inline)) -> uint8_t* {
+    return x == 0 ? qs0 : x == 1 ? qs1 : x == 2 ? qs2 : qs3;
+  };
+  auto gslot = [&](int x) __attribute__((always_inline)) -> uint8_t* {
+    return x == 0 ? gs0 : x == 1 ? gs1 : x == 2 ? gs2 : gs3;
+  };
+  auto lslot = [&](int x) __attribute__((always_inline)) -> float* {
+    return x == 0 ? ls0 : x == 1 ? ls1 : x == 2 ? ls2 : ls3;
+  };
+  auto dslot = [&](int x) __attribute__((always_inline)) -> float* {
+    return x == 0 ? ds0 : x == 1 ? ds1 : x == 2 ? ds2 : ds3;
+  };
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int c = lane & 31;
 
   // Key blocks in ascending order: under the causal mask the first blocks
   // are seen by the most query tiles, so the heaviest work starts first.
-  const int gsi = blockIdx.x % a.gsplit;   // which share of the head group
+  const int gsi = blockIdx.x % a.gsplit;  // which share of the head group
   const int rest = blockIdx.x / a.gsplit;
   const int kt = rest / a.n_bk;
   const int bk = rest % a.n_bk;
@@ -183,10 +308,9 @@ __global__ __launch_bounds__(NTB, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs 
   const int kw0 = kblk0 + wave * 32;  // first key of this wave
   const int my_key = kw0 + c;         // the key this lane's column holds
 
+  // Stationary K and V as B operands: lane holds row my_key, dims 16kc + 8h.
   const uint16_t* kbase = a.k + (size_t)bk * Nkv * D;
   const uint16_t* vbase = a.v + (size_t)bk * Nkv * D;
-
-  // Stationary K and V as B operands: lane holds row my_key, dims 16kc + 8h.
   V8 kf[KC], vf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -202,7 +326,7 @@ __global__ __launch_bounds__(NTB, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs 
   }
 
   // Query tiles that can see some key of this block, for each of this
-  // workgroup's query heads, flattened into one loop.
+  // workgroup's query heads, flattened into one sequence.
   const int n_qt = (Nq + BQ - 1) / BQ;
   int qt_begin = 0;
   if (CAUSAL) {
@@ -214,83 +338,97 @@ __global__ __launch_bounds__(NTB, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs 
   const int total = per_head * heads;
   const int hq0 = hkv * a.G + gsi * heads;
 
-  QTileRegs<D> regs;
+  const uint32_t src = k_dma_src<D, 4>(wave, lane);
+  const uint32_t kr0 = k_read_base<D>(h, c, 0);
+  const uint32_t kr1 = k_read_base<D>(h, c, 1);
+  const uint32_t kt0 = kt_read_base<D>(h, c, 0);
+  const uint32_t kt1 = kt_read_base<D>(h, c, 1);
+  const uint32_t q_bytes = (uint32_t)Nq * D * 2u;
+  const uint32_t row_bytes = (uint32_t)Nq * 4u;
+  // Tile t (query head, first row) into slot x: Q and dO rows (reads past
+  // N_q fill zeros, which add nothing to dK, dV), LSE2 and D rows.
+  auto load_tile = [&](int t, int x) __attribute__((always_inline)) {
+    if (t >= total) return;
+    const int hq = hq0 + t / per_head;
+    const int qi0 = (qt_begin + t % per_head) * BQ;
+    const size_t rb = (size_t)b * a.Hq + hq;
+    dma_tile<D, 4>(qslot(x), a.q + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
+    dma_tile<D, 4>(gslot(x), a.dO + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
+    if (wave < 2) {
+      const float* rows = (wave == 0 ? a.lse2 : a.delta) + rb * Nq + qi0;
+      const uint32_t left = row_bytes - __builtin_amdgcn_readfirstlane(min(row_bytes, (uint32_t)qi0 * 4u));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          make_rsrc(rows, left),
+          (__attribute__((address_space(3))) void*)(wave == 0 ? lslot(x) : dslot(x)), 4,
+          (uint32_t)lane * 4u, 0, 0, 0);
+    }
+  };
+  // Mask tile t's scores s where a key is past the end or, when causal,
+  // after the query's limit.
+  auto mask_tile = [&](int t, f32x16* s) __attribute__((always_inline)) {
+    const int qi0 = (qt_begin + t % per_head) * BQ;
+    const bool need_mask = (kw0 + 32 > Nkv) || (CAUSAL && kw0 + 31 > qi0 + offset);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bool vis = my_key < Nkv;
+          if (CAUSAL) vis = vis && (my_key <= qi0 + qb * 32 + acc_key(h, r) + offset);
+          s[qb][r] = vis ? s[qb][r] : -INFINITY;
+        }
+    }
+  };
+
+  // Pipeline state entering step i: scores and dP of tile i, P and dS of tile
+  // i - 1. Tile t's scores live in sa/da and its P, dS in pa/za when t is
+  // even, in sb/db and pb/zb when t is odd.
+  f32x16 sa[2], da[2], sb[2], db[2];
+  uint32_t pa[16], za[16], pb[16], zb[16];
+  const float sl2 = a.scale_log2;
+
+  // Prologue: tiles 0 and 1; scores of tile 0; step 0 (no tile -1).
+  load_tile(0, 0);
+  load_tile(1, 1);
+  __syncthreads();
   if (total > 0) {
-    const size_t rb = ((size_t)b * a.Hq + hq0) * Nq;
-    load_q_tile<D>(regs, a.q + rb * D, a.dO + rb * D, a.lse + rb, a.delta + rb, qt_begin * BQ, Nq, tid);
-    store_q_tile<D>(regs, sm + L::Q_OFF, sm + L::DO_OFF, lse_s[0], del_s[0], tid);
+    tile_rows<T, D>(qs0, kr0, kr1, kf, sa);
+    tile_rows<T, D>(gs0, kr0, kr1, vf, da);
+    load_tile(2, 2);
+    mask_tile(0, sa);
+    dkdv_step<T, D, false>(qs1, gs1, qs3, gs3, kr0, kr1, kt0, kt1, kf, vf, sb, db, dk, dv, pb, zb,
+                           sa, da, ls0, ds0, h, sl2, pa, za);
   }
   __syncthreads();
 
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
-    const int hq = hq0 + it / per_head;
-    const int qi0 = (qt_begin + it % per_head) * BQ;
-    const size_t rowbase = ((size_t)b * a.Hq + hq) * Nq;
-    const bool more = it + 1 < total;
-    if (more) {
-      const int hq_n = hq0 + (it + 1) / per_head;
-      const int qi_n = (qt_begin + (it + 1) % per_head) * BQ;
-      const size_t rb = ((size_t)b * a.Hq + hq_n) * Nq;
-      load_q_tile<D>(regs, a.q + rb * D, a.dO + rb * D, a.lse + rb, a.delta + rb, qi_n, Nq, tid);
-    }
-    const uint16_t* qs = sm + L::Q_OFF + buf * L::TILE;
-    const uint16_t* gs = sm + L::DO_OFF + buf * L::TILE;
-    const float* ls = lse_s[buf];
-    const float* ds_ = del_s[buf];
-
-    // ---- S = Q K^T and dP = dO V^T (rows: query, columns: this wave's keys)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = zero16();
-      dp[qb] = zero16();
-      const uint16_t* qrow = qs + (qb * 32 + row_perm(c)) * L::RS + h * 8;
-      const uint16_t* grow = gs + (qb * 32 + row_perm(c)) * L::RS + h * 8;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(qrow + kc * 16)), kf[kc], s[qb]);
-        dp[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(grow + kc * 16)), vf[kc], dp[qb]);
+  // Step i: tile i + 2 loads into slot (i + 2) % 4, whose tile i - 2 was
+  // last read in step i - 1 (every wave passed the barrier that ended it);
+  // the step reads slots (i + 1) % 4 (rows), i % 4 (LSE2, D) and
+  // (i - 1) % 4 (transposed). With i = 1 + 4 n + r every slot and array is
+  // named statically.
+  for (int i0 = 1; i0 < total; i0 += 4) {
+    static_for<4>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
+      constexpr bool even = (r & 1) == 1;  // is tile i = i0 + r even?
+      const int i = i0 + r;
+      if (i < total) {
+        load_tile(i + 2, (r + 3) & 3);
+        f32x16* s = even ? sa : sb;
+        f32x16* dpc = even ? da : db;
+        mask_tile(i, s);
+        dkdv_step<T, D, true>(qslot((r + 2) & 3), gslot((r + 2) & 3), qslot(r & 3), gslot(r & 3),
+                              kr0, kr1, kt0, kt1, kf, vf, even ? sb : sa, even ? db : da, dk, dv,
+                              even ? pb : pa, even ? zb : za, s, dpc, lslot((r + 1) & 3),
+                              dslot((r + 1) & 3), h, sl2, even ? pa : pb, even ? za : zb);
+        __syncthreads();
       }
-    }
-    // ---- P = exp(scale S - LSE), dS = P (dP - D); masks only where needed.
-    const bool need_mask = (kw0 + 32 > Nkv) || (CAUSAL && kw0 + 31 > qi0 + offset);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lq = qb * 32 + acc_key(h, r);
-        float p = __builtin_amdgcn_exp2f(fmaf(s[qb][r], a.scale_log2, -ls[lq]));
-        if (need_mask) {
-          bool vis = my_key < Nkv;
-          if (CAUSAL) vis = vis && (my_key <= qi0 + lq + offset);
-          p = vis ? p : 0.0f;
-        }
-        s[qb][r] = p;
-        dp[qb][r] = p * (dp[qb][r] - ds_[lq]);
-      }
-    // ---- dV^T += dO^T P and dK^T += Q^T dS (contraction over the BQ queries);
-    // the transposed operands come from transposed LDS reads.
-#pragma unroll
-    for (int ch = 0; ch < BQ / 16; ++ch) {
-      float pv[8], dv8[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-        dv8[t] = dp[ch >> 1][(ch & 1) * 8 + t];
-      }
-      const V8 pf = pack8<T>(pv);
-      const V8 dsf = pack8<T>(dv8);
-#pragma unroll
-      for (int od = 0; od < OD; ++od) {
-        dv[od] = T::mfma(load_vt_operand<T, L::RS>(gs, h, c, ch * 16, od * 32), pf, dv[od]);
-        dk[od] = T::mfma(load_vt_operand<T, L::RS>(qs, h, c, ch * 16, od * 32), dsf, dk[od]);
-      }
-    }
-    if (more)
-      store_q_tile<D>(regs, sm + L::Q_OFF + (buf ^ 1) * L::TILE, sm + L::DO_OFF + (buf ^ 1) * L::TILE,
-                      lse_s[buf ^ 1], del_s[buf ^ 1], tid);
-    __syncthreads();
+    });
+  }
+  // The last tile's dV, dK.
+  if (total > 0) {
+    const int x = (total - 1) & 3;
+    const bool odd = (total - 1) & 1;
+    dkdv_tail<T, D>(qslot(x), gslot(x), kt0, kt1, dk, dv, odd ? pb : pa, odd ? zb : za);
   }
 
   // ---- dK = scale * (sum dS^T Q) and dV (lane = key, 16 dims per tile); a
@@ -376,6 +514,7 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.dO = static_cast<const uint16_t*>(t.dO);
   a.dk = static_cast<uint16_t*>(t.dk);
   a.dv = static_cast<uint16_t*>(t.dv);
+  a.lse2 = t.lse2;
   a.delta = t.delta;
   a.dk_part = t.dk_part;
   a.dv_part = t.dv_part;
@@ -399,8 +538,8 @@ hipError_t pre_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   constexpr int RPB = NTB / (D / 8);
   dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, dim3(NTB), 0, stream,
-                     static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.delta,
-                     rows);
+                     static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.lse,
+                     t.delta, t.lse2, rows);
   return hipGetLastError();
 }
 
@@ -410,9 +549,9 @@ hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   if (a.n_kblocks == 0 || a.n_bk == 0) return hipSuccess;
   dim3 grid((unsigned)(a.n_kblocks * a.n_bk * a.gsplit));
   if (p.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<T, D, true>), grid, dim3(NTB), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, dim3(NTB), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<T, D, false>), grid, dim3(NTB), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, dim3(NTB), 0, stream, a);
   return hipGetLastError();
 }
 

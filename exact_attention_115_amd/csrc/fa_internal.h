@@ -38,6 +38,7 @@ struct BwdPtrs {
   void* dk;
   void* dv;
   float* delta;      // [B, Hq, Nq] float32, in the workspace
+  float* lse2;       // [B, Hq, Nq] float32 LSE * log2(e), in the workspace
   float* dk_part;    // [gsplit, B, Hkv, Nkv, d] float32 partial sums, or NULL
   float* dv_part;    //   (present only when the head group is split)
 };

@@ -53,14 +53,14 @@ def test_workspace_sizes():
     assert ws > 0 and ws % 256 == 0
     rows = ws // (129 * 4)
     assert rows % (16 * 32) == 0
-    # Backward: the float32 row terms D, linear in N.
+    # Backward: the float32 row terms D and LSE log2(e), linear in N.
     for B, Hq, Hkv, N, d in [(1, 32, 32, 4096, 128), (2, 16, 16, 1024, 64), (4, 32, 8, 2048, 128)]:
-        want = _align(B * Hq * N * 4)
+        want = 2 * _align(B * Hq * N * 4)
         assert lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) == want
     # MQA with few key blocks: the head group is split over s workgroups, which
     # adds float32 partial dK and dV planes (s of each), s a divisor of G.
     B, Hq, Hkv, N, d = 4, 32, 1, 2048, 128
-    base = _align(B * Hq * N * 4)
+    base = 2 * _align(B * Hq * N * 4)
     extra = lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) - base
     plane = B * Hkv * N * d * 4
     assert extra > 0 and extra % (2 * plane) == 0
