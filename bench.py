@@ -1,17 +1,27 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-fa_fwd (forward kernel) followed by fa_bwd's three stages (D_i and clearing
-the dQ accumulator, the key/value-stationary gradient kernel, dQ rounding),
-all through the C ABI on torch's current stream, inputs resident in HBM.
+fa_fwd (the forward kernel) followed by fa_bwd's three stages (the row terms
+D_i and LSE_i log2(e); the key-block kernel computing dK and dV; the
+query-tile kernel computing dQ), all through the C ABI on torch's current
+stream, inputs resident in HBM.
 
 Default workload: causal attention B=1, Hq=Hkv=32, N=4096, d=128, bf16
 (the pages' 4096-token, 32-head case). ``value`` is the step's algorithmic
 throughput: forward 4*B*Hq*N_q*N_kv*d FLOP, backward 2.5x that, both halved
 for causal, divided by the measured time per step.
 
+The roofline objects price each kernel's algorithmic FLOP per launch against
+the published bf16/fp16 dense matrix-core peak. The backward's five products
+of two N x d operands (S, dP, dV, dK, dQ) split as four in the key-block
+kernel and one (dQ = dS K) in the query-tile kernel; the S and dP that the
+query-tile kernel recomputes are an implementation cost and are not counted.
+
 Prints ONE JSON line. ``--workload`` selects another synthetic workload for
 development measurements (decode workloads report HBM GB/s).
+``--copy-mib M`` runs one plain device copy of M MiB before the warmup, so a
+rocprofv3 counter run of this command also holds a copy kernel of known size
+to calibrate FETCH_SIZE / WRITE_SIZE against.
 """
 
 from __future__ import annotations
@@ -31,10 +41,20 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 METRIC = "attention fwd/bwd TFLOP/s & % bf16 MFMA peak, causal N=4096 d=128"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "bwd_main_c3_traffic.md")
+CSRC = os.path.join(ROOT, "exact_attention_115_amd", "csrc")
+COMMON = ["fa_device.h", "fa_tile.h", "fa_internal.h"]
+# Sources each kernel is built from; a counter summary is only used while
+# their hash matches the one it was taken on.
 KERNEL_SOURCES = {
-    "fwd": os.path.join(ROOT, "exact_attention_115_amd", "csrc", "fa_fwd.hip"),
-    "bwd_main": os.path.join(ROOT, "exact_attention_115_amd", "csrc", "fa_bwd.hip"),
+    "fwd": ["fa_fwd.hip"] + COMMON,
+    "bwd_pre": ["fa_bwd.hip"] + COMMON,
+    "bwd_dkdv": ["fa_bwd.hip"] + COMMON,
+    "bwd_dq": ["fa_bwd_dq.hip"] + COMMON,
+}
+TRAFFIC_SUMMARY = {
+    "fwd": "fwd_causal_b1h32n4096d128_bf16_hbm_traffic.md",
+    "bwd_dkdv": "bwd_dkdv_causal_b1h32n4096d128_bf16_hbm_traffic.md",
+    "bwd_dq": "bwd_dq_causal_b1h32n4096d128_bf16_hbm_traffic.md",
 }
 
 
@@ -47,24 +67,31 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the warmup")
     return ap.parse_args()
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(kernel_key):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel_key]:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the summary is missing or was taken on another kernel source."""
-    if not os.path.exists(PROFILE_SUMMARY):
+    name = TRAFFIC_SUMMARY.get(kernel_key)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
         return None
-    text = open(PROFILE_SUMMARY).read()
+    text = open(path).read()
     m_hash = re.search(r"source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
     m_bytes = re.search(r"HBM bytes per launch:\s*`?([0-9.eE+]+)", text)
     if not m_hash or not m_bytes:
         return None
-    if m_hash.group(1) != source_hash(KERNEL_SOURCES[kernel_key]):
+    if m_hash.group(1) != source_hash(kernel_key):
         return None
     return float(m_bytes.group(1))
 
@@ -72,8 +99,6 @@ def read_traffic(kernel_key):
 def cpu_baseline(w, budget_s):
     """Time the float64 oracle (as it stands) on a bounded sample of whole
     heads of the workload; returns the throughput in the bench's unit."""
-    import numpy as np
-
     import oracle
     from synth import make_inputs, to_f64
 
@@ -115,6 +140,14 @@ def decode_bytes(w):
             + 4 * w.B * w.Hq * w.Nq)
 
 
+def mfma_roofline(kernel, flop, ms, traffic):
+    ach = flop / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "kernel": kernel, "avg_launch_ms": round(ms, 4),
+            "algorithmic_flop_per_launch": flop}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,6 +163,15 @@ def main():
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     q, k, v, do = make_inputs(w)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     do = do.to(dev) if do is not None else None
@@ -142,9 +184,8 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         bws = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, q.dtype)
         bwd_ws = torch.empty(bws, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
-    names = ["fwd"] + (["bwd_pre", "bwd_main", "bwd_dq"] if bwd else [])
+    names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if bwd else [])
 
     def step(events=None):
         if events is not None:
@@ -220,20 +261,20 @@ def main():
                     "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                     "fwd_tflops": round(fwd_t, 2),
                     "fwd_pct_peak": round(100 * fwd_t / PEAK_BF16_TFLOPS, 2)})
+        flop = {"fwd": fwd_flop}
         if bwd:
-            bwd_ms = per_kernel_ms["bwd_pre"] + per_kernel_ms["bwd_main"] + per_kernel_ms["bwd_dq"]
+            bwd_ms = per_kernel_ms["bwd_pre"] + per_kernel_ms["bwd_dkdv"] + per_kernel_ms["bwd_dq"]
             bwd_t = bwd_flop / (bwd_ms * 1e-3) / 1e12
             out.update({"bwd_tflops": round(bwd_t, 2), "bwd_pct_peak": round(100 * bwd_t / PEAK_BF16_TFLOPS, 2)})
-        # Roofline of the dominant kernel (the longest average launch).
-        dom = max(per_kernel_ms, key=per_kernel_ms.get)
-        flop = {"fwd": fwd_flop, "bwd_main": bwd_flop}.get(dom)
-        if flop is not None:
-            ach = flop / (per_kernel_ms[dom] * 1e-3) / 1e12
-            out["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                               "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                               "traffic": read_traffic(dom) if args.workload == "c3" else None,
-                               "kernel": dom, "avg_launch_ms": round(per_kernel_ms[dom], 4),
-                               "algorithmic_flop_per_launch": flop}
+            flop.update({"bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop})
+        on_profiled = args.workload == "c3"
+        lines = {kname: mfma_roofline(kname, f, per_kernel_ms[kname],
+                                      read_traffic(kname) if on_profiled else None)
+                 for kname, f in flop.items()}
+        # The dominant kernel is the one with the longest average launch.
+        dom = max(lines, key=lambda kname: per_kernel_ms[kname])
+        out["roofline"] = lines[dom]
+        out["roofline_all"] = lines
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
