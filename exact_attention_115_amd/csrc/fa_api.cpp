@@ -160,8 +160,8 @@ BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, 
   const size_t rows = (size_t)p.B * p.Hq * p.Nq;
   const size_t del = align_up(rows * sizeof(float), 256);
   char* base = static_cast<char*>(ws);
-  t.delta = reinterpret_cast<float*>(base);
-  t.lse2 = base ? reinterpret_cast<float*>(base + del) : nullptr;
+  t.nd = reinterpret_cast<float*>(base);
+  t.lneg = base ? reinterpret_cast<float*>(base + del) : nullptr;
   t.dk_part = t.dv_part = nullptr;
   const int gs = bwd_group_split(p);
   if (gs > 1 && base) {

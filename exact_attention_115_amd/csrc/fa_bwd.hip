@@ -11,7 +11,8 @@
 // (D_i equals sum_j P_ij dP_ij because O = P V.)
 //
 // Three stages on one stream:
-//   0  pre:   D_i for every query row (float32, in the workspace).
+//   0  pre:   -D_i and -LSE_i / scale for every query row (float32, in the
+//             workspace): the starting values of the dP and S accumulators.
 //   1  dK/dV: one workgroup per 128-key block of one (b, kv head). K and V of
 //             the block stay in registers; the workgroup loops over the query
 //             heads of the group (GQA/MQA: dK, dV summed in registers, no
@@ -55,8 +56,8 @@ struct BwdArgs {
   const uint16_t* dO;
   uint16_t* dk;
   uint16_t* dv;
-  const float* lse2;   // LSE * log2(e) per query row (+inf: row saw no key)
-  float* delta;
+  const float* lneg;   // -LSE / scale per query row (-inf: row saw no key)
+  float* nd;           // -D per query row
   float* dk_part;
   float* dv_part;
   int Hq, Hkv, G, Nq, Nkv, n_kblocks, n_bk, gsplit;
@@ -64,14 +65,18 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------- stage 0
-// D_i = sum_c dO_ic O_ic in float32, and LSE2_i = LSE_i log2(e) (+inf for a
-// row that saw no key, so that exp2(S scale log2(e) - LSE2) = P is 0).
+// nd_i = -D_i = -sum_c dO_ic O_ic in float32, and lneg_i = -LSE_i / scale
+// (-inf for a row that saw no key). Starting the S accumulator of row i at
+// lneg_i and the dP accumulator at nd_i leaves S - LSE / scale and dP - D in
+// them, so P = exp2(scale log2(e) acc) and dS = P acc' need no further
+// per-row terms.
 template <typename T, int D>
 __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ lse2, size_t rows) {
+                                                      float* __restrict__ nd,
+                                                      float* __restrict__ lneg, size_t rows,
+                                                      float inv_scale) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int RPB = NTB / CPR;
   const int t = threadIdx.x;
@@ -90,21 +95,39 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && ch == 0) {
-    delta[row] = acc;
+    nd[row] = -acc;
     const float l = lse[row];
-    lse2[row] = l == -INFINITY ? INFINITY : l * LOG2E;
+    lneg[row] = l == -INFINITY ? -INFINITY : -l * inv_scale;
   }
 }
 
 // ---------------------------------------------------------------- stage 1
+// Accumulator start values from a tile's per-row terms x (64 floats in LDS):
+// accumulator r of block qb holds query row qb * 32 + acc_key(h, r), two
+// runs of eight consecutive rows per block.
+__device__ __forceinline__ void init_rows(const float* x, int h, f32x16* acc) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + qb * 32 + run * 16 + 8 * h + 4 * half);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[qb][run * 8 + half * 4 + j] = v[j];
+      }
+}
+
 // One step of the dK/dV pipeline for query tile i, as a single interleaved
 // instruction stream of three independent parts:
 //   * scores and dP of tile i + 1: sn = Q' K^T, dpn = dO' V^T (rows of the
 //     next Q / dO tiles read from LDS; K, V stationary B operands)
 //   * dV^T += dO^T P and dK^T += Q^T dS of tile i - 1 (PREV; transposed LDS
 //     reads of that tile's Q / dO, its P and dS already rounded in pp, dsp)
-//   * P = exp2(S scale_log2 - LSE2) and dS = P (dP - D) of tile i, rounded
-//     to 16 bits into pc, dsc (lse / dl: the tile's LSE2 and D rows in LDS)
+//   * P = exp2(scale_log2 S') and dS = P dP' of tile i, rounded to 16 bits
+//     into pc, dsc, where S' = S - LSE / scale and dP' = dP - D: the
+//     accumulators of tile i + 1 start from its rows' -LSE / scale and -D
+//     (ln, dn: those rows in LDS)
 // Matrix-core products alternate between row and transposed products; LDS
 // operands are read two products of their kind ahead; scheduling fences keep
 // the order. Element pair e of a lane is keys' query rows 32 (e / 8) +
@@ -115,7 +138,7 @@ __device__ __forceinline__ void dkdv_step(
     const uint8_t* qn, const uint8_t* gn, const uint8_t* qp, const uint8_t* gp, uint32_t kr0,
     uint32_t kr1, uint32_t kt0, uint32_t kt1, const typename T::vec8* kf, const typename T::vec8* vf,
     f32x16* sn, f32x16* dpn, f32x16* dk, f32x16* dv, const uint32_t* pp, const uint32_t* dsp,
-    const f32x16* s, const f32x16* dpc, const float* lse, const float* dl, int h, float sl2,
+    const f32x16* s, const f32x16* dpc, const float* ln, const float* dn, int h, float sl2,
     uint32_t* pc, uint32_t* dsc) {
   using V8 = typename T::vec8;
   constexpr int RB = DmaTile<D>::RB;
@@ -134,10 +157,8 @@ __device__ __forceinline__ void dkdv_step(
     const int y = t & 1, ch = (t >> 1) / OD, od = (t >> 1) % OD;
     return load_kt_dma<T, D>(y ? qp : gp, kt0, kt1, ch, od);
   };
-  sn[0] = zero16();
-  sn[1] = zero16();
-  dpn[0] = zero16();
-  dpn[1] = zero16();
+  init_rows(ln, h, sn);
+  init_rows(dn, h, dpn);
   u32x4 rf[NR];
   V8 tf[NT];
   rf[0] = rfrag(0);
@@ -180,17 +201,14 @@ __device__ __forceinline__ void dkdv_step(
       const int pidx = m * PARTS + u;
       const int e = pidx >> 2, part = pidx & 3;
       const int kb = e >> 3, r = 2 * (e & 7);
-      const int q = kb * 32 + acc_key(h, r);
       if (part == 0) {
-        const float2 l2 = *reinterpret_cast<const float2*>(lse + q);
-        e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -l2.x));
-        e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -l2.y));
+        e0 = __builtin_amdgcn_exp2f(s[kb][r] * sl2);
+        e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] * sl2);
       } else if (part == 1) {
         pc[e] = pack2<T>(e0, e1);
       } else if (part == 2) {
-        const float2 d2 = *reinterpret_cast<const float2*>(dl + q);
-        e0 = e0 * (dpc[kb][r] - d2.x);
-        e1 = e1 * (dpc[kb][r + 1] - d2.y);
+        e0 = e0 * dpc[kb][r];
+        e1 = e1 * dpc[kb][r + 1];
       } else {
         dsc[e] = pack2<T>(e0, e1);
       }
@@ -227,12 +245,13 @@ __device__ __forceinline__ void dkdv_tail(const uint8_t* qp, const uint8_t* gp, 
 // K-layout tile xs and the stationary B operand xf.
 template <typename T, int D>
 __device__ __forceinline__ void tile_rows(const uint8_t* xs, uint32_t kb0, uint32_t kb1,
-                                          const typename T::vec8* xf, f32x16* s) {
+                                          const typename T::vec8* xf, const float* x0, int h,
+                                          f32x16* s) {
   constexpr int RB = DmaTile<D>::RB;
   constexpr int KC = D / 16;
+  init_rows(x0, h, s);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    s[qb] = zero16();
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const uint8_t* p = xs + ((kc & 1) ? kb1 : kb0) + qb * 32 * RB + (kc >> 1) * 1024;
@@ -251,9 +270,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // One workgroup of 4 waves per 128-key block (32 keys per wave) of one
 // (b, kv head) and one share of the head group. Q / dO tiles of BQ = 64 rows
-// (and their LSE2, D rows) go through a ring of 4 LDS slots filled by direct
+// (and their -LSE / scale, -D rows) go through a ring of 4 LDS slots filled by direct
 // global -> LDS loads two tiles ahead; step i reads tile i + 1 (rows), tile
-// i (LSE2, D) and tile i - 1 (transposed). One wave per SIMD: the stationary
+// i + 1 (row terms) and tile i - 1 (transposed). One wave per SIMD: the stationary
 // K, V, the dK, dV accumulators and two tiles of scores and P need more than
 // the 256 registers two waves per SIMD would leave.
 template <typename T, int D, bool CAUSAL>
@@ -346,7 +365,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t q_bytes = (uint32_t)Nq * D * 2u;
   const uint32_t row_bytes = (uint32_t)Nq * 4u;
   // Tile t (query head, first row) into slot x: Q and dO rows (reads past
-  // N_q fill zeros, which add nothing to dK, dV), LSE2 and D rows.
+  // N_q fill zeros, which add nothing to dK, dV), -LSE / scale and -D rows.
   auto load_tile = [&](int t, int x) __attribute__((always_inline)) {
     if (t >= total) return;
     const int hq = hq0 + t / per_head;
@@ -355,7 +374,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dma_tile<D, 4>(qslot(x), a.q + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
     dma_tile<D, 4>(gslot(x), a.dO + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
     if (wave < 2) {
-      const float* rows = (wave == 0 ? a.lse2 : a.delta) + rb * Nq + qi0;
+      const float* rows = (wave == 0 ? a.lneg : a.nd) + rb * Nq + qi0;
       const uint32_t left = row_bytes - __builtin_amdgcn_readfirstlane(min(row_bytes, (uint32_t)qi0 * 4u));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           make_rsrc(rows, left),
@@ -392,18 +411,18 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   load_tile(1, 1);
   __syncthreads();
   if (total > 0) {
-    tile_rows<T, D>(qs0, kr0, kr1, kf, sa);
-    tile_rows<T, D>(gs0, kr0, kr1, vf, da);
+    tile_rows<T, D>(qs0, kr0, kr1, kf, ls0, h, sa);
+    tile_rows<T, D>(gs0, kr0, kr1, vf, ds0, h, da);
     load_tile(2, 2);
     mask_tile(0, sa);
     dkdv_step<T, D, false>(qs1, gs1, qs3, gs3, kr0, kr1, kt0, kt1, kf, vf, sb, db, dk, dv, pb, zb,
-                           sa, da, ls0, ds0, h, sl2, pa, za);
+                           sa, da, ls1, ds1, h, sl2, pa, za);
   }
   __syncthreads();
 
   // Step i: tile i + 2 loads into slot (i + 2) % 4, whose tile i - 2 was
   // last read in step i - 1 (every wave passed the barrier that ended it);
-  // the step reads slots (i + 1) % 4 (rows), i % 4 (LSE2, D) and
+  // the step reads slots (i + 1) % 4 (rows and row terms) and
   // (i - 1) % 4 (transposed). With i = 1 + 4 n + r every slot and array is
   // named statically.
   for (int i0 = 1; i0 < total; i0 += 4) {
@@ -418,8 +437,8 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
         mask_tile(i, s);
         dkdv_step<T, D, true>(qslot((r + 2) & 3), gslot((r + 2) & 3), qslot(r & 3), gslot(r & 3),
                               kr0, kr1, kt0, kt1, kf, vf, even ? sb : sa, even ? db : da, dk, dv,
-                              even ? pb : pa, even ? zb : za, s, dpc, lslot((r + 1) & 3),
-                              dslot((r + 1) & 3), h, sl2, even ? pa : pb, even ? za : zb);
+                              even ? pb : pa, even ? zb : za, s, dpc, lslot((r + 2) & 3),
+                              dslot((r + 2) & 3), h, sl2, even ? pa : pb, even ? za : zb);
         __syncthreads();
       }
     });
@@ -514,8 +533,8 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.dO = static_cast<const uint16_t*>(t.dO);
   a.dk = static_cast<uint16_t*>(t.dk);
   a.dv = static_cast<uint16_t*>(t.dv);
-  a.lse2 = t.lse2;
-  a.delta = t.delta;
+  a.lneg = t.lneg;
+  a.nd = t.nd;
   a.dk_part = t.dk_part;
   a.dv_part = t.dv_part;
   a.gsplit = bwd_group_split(p);
@@ -539,7 +558,7 @@ hipError_t pre_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, dim3(NTB), 0, stream,
                      static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.lse,
-                     t.delta, t.lse2, rows);
+                     t.nd, t.lneg, rows, 1.0f / p.scale);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ struct DqArgs {
   const uint16_t* v;
   const uint16_t* dO;
   const float* lse;
-  const float* delta;
+  const float* nd;  // -D per query row
   uint16_t* dq;
   int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
   float scale, scale_log2;
@@ -128,11 +128,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
     qf[kc] = as_vec8<T>(has_row ? ld16(qp + kc * 16 + h * 8) : zero_u32x4());
     gf[kc] = as_vec8<T>(has_row ? ld16(gp + kc * 16 + h * 8) : zero_u32x4());
   }
-  float lse2 = INFINITY, drow = 0.0f;
+  float lse2 = INFINITY, ndrow = 0.0f;
   if (has_row) {
     const float l = a.lse[bh * Nq + qrow];
     if (l != -INFINITY) lse2 = l * LOG2E;
-    drow = a.delta[bh * Nq + qrow];
+    ndrow = a.nd[bh * Nq + qrow];
   }
   const float sl2 = a.scale_log2;
 
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
       const int kb = i >> 3, r = 2 * (i & 7);
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -lse2));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -lse2));
-      ds[i] = pack2<T>(p0 * (dp[kb][r] - drow), p1 * (dp[kb][r + 1] - drow));
+      ds[i] = pack2<T>(p0 * (dp[kb][r] + ndrow), p1 * (dp[kb][r + 1] + ndrow));
     }
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
@@ -218,7 +218,7 @@ hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   a.v = static_cast<const uint16_t*>(t.v);
   a.dO = static_cast<const uint16_t*>(t.dO);
   a.lse = t.lse;
-  a.delta = t.delta;
+  a.nd = t.nd;
   a.dq = static_cast<uint16_t*>(t.dq);
   a.B = p.B;
   a.Hq = p.Hq;

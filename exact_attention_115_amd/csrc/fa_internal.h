@@ -37,8 +37,8 @@ struct BwdPtrs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;      // [B, Hq, Nq] float32, in the workspace
-  float* lse2;       // [B, Hq, Nq] float32 LSE * log2(e), in the workspace
+  float* nd;         // [B, Hq, Nq] float32 -D, in the workspace
+  float* lneg;       // [B, Hq, Nq] float32 -LSE / scale (-inf: no key), in the workspace
   float* dk_part;    // [gsplit, B, Hkv, Nkv, d] float32 partial sums, or NULL
   float* dv_part;    //   (present only when the head group is split)
 };
