@@ -371,8 +371,8 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int hq = hq0 + t / per_head;
     const int qi0 = (qt_begin + t % per_head) * BQ;
     const size_t rb = (size_t)b * a.Hq + hq;
-    dma_tile<D, 4>(qslot(x), a.q + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
-    dma_tile<D, 4>(gslot(x), a.dO + rb * Nq * D, q_bytes, qi0, wave, src, DT::K_STEP);
+    dma_tile<D, 4, DT::K_STEP>(qslot(x), a.q + rb * Nq * D, q_bytes, qi0, wave, src);
+    dma_tile<D, 4, DT::K_STEP>(gslot(x), a.dO + rb * Nq * D, q_bytes, qi0, wave, src);
     if (wave < 2) {
       const float* rows = (wave == 0 ? a.lneg : a.nd) + rb * Nq + qi0;
       const uint32_t left = row_bytes - __builtin_amdgcn_readfirstlane(min(row_bytes, (uint32_t)qi0 * 4u));

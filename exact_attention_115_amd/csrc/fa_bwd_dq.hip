@@ -114,8 +114,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   const uint32_t kt0 = kt_read_base<D>(h, c, 0);
   const uint32_t kt1 = kt_read_base<D>(h, c, 1);
   auto load_kv = [&](int j, uint8_t* kd, uint8_t* vd) __attribute__((always_inline)) {
-    dma_tile<D, NW>(kd, khead, kv_bytes, j * BC, wave, src, DT::K_STEP);
-    dma_tile<D, NW>(vd, vhead, kv_bytes, j * BC, wave, src, DT::K_STEP);
+    dma_tile<D, NW, DT::K_STEP>(kd, khead, kv_bytes, j * BC, wave, src);
+    dma_tile<D, NW, DT::K_STEP>(vd, vhead, kv_bytes, j * BC, wave, src);
   };
 
   // Q and dO of this lane's row as B operands; its LSE (log2 units; +inf for

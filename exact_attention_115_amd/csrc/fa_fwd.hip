@@ -257,10 +257,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   const uint32_t vr = v_read_base<D>(h, c);
   constexpr int KS = DT::K_STEP, VS = DT::V_STEP;
   auto load_k = [&](int j, uint8_t* dst) __attribute__((always_inline)) {
-    dma_tile<D, NW>(dst, khead, kv_bytes, j * BC, wave, k_src, KS);
+    dma_tile<D, NW, KS>(dst, khead, kv_bytes, j * BC, wave, k_src);
   };
   auto load_v = [&](int j, uint8_t* dst) __attribute__((always_inline)) {
-    dma_tile<D, NW>(dst, vhead, kv_bytes, j * BC, wave, v_src, VS);
+    dma_tile<D, NW, VS>(dst, vhead, kv_bytes, j * BC, wave, v_src);
   };
 
   // Q^T as the B operand: lane holds Q[qrow][16 kc + 8h .. +7].

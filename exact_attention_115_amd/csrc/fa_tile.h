@@ -166,22 +166,35 @@ __device__ inline uint32_t v_dma_src(int wave, int l) {
 
 // Issue this wave's DMA loads of one K (or V) tile: `tile` is the tile's LDS
 // base, `head` the global base of the head's K (or V), `head_bytes` its size,
-// `key0` the tile's first key. Reads past the head's end fill zeros.
-template <int D, int NW>
-__device__ inline void dma_tile(uint8_t* tile, const uint16_t* head, uint32_t head_bytes, int key0,
-                                int wave, uint32_t lane_src, int step) {
+// `key0` the tile's first key; block i of the wave reads from STEP * i bytes
+// past the lane's source (K_STEP or V_STEP). One buffer resource covers the
+// tile: it starts at the tile and ends at the head's end, so reads past the
+// end fill zeros; the blocks differ only in the instruction's offset field.
+template <int D, int NW, int STEP, int I = 0>
+__device__ __forceinline__ void dma_blocks(__amdgpu_buffer_rsrc_t r, uint8_t* tile, int wave,
+                                           uint32_t lane_src) {
   using T = DmaTile<D, NW>;
-#pragma unroll
-  for (int i = 0; i < T::PER_WAVE; ++i) {
-    const uint32_t start = (uint32_t)key0 * T::RB + (uint32_t)(i * step);
-    // Scalar arithmetic (min then subtract) keeps the resource in SGPRs.
-    const uint32_t left = head_bytes - __builtin_amdgcn_readfirstlane(min(head_bytes, start));
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(reinterpret_cast<const uint8_t*>(head) + start, left);
+  if constexpr (I < T::PER_WAVE) {
+    // The offset field is added to the LDS address as well as to the
+    // memory address: the LDS base is lowered by as much.
+    static_assert(I * STEP < 4096 && I * STEP <= I * 1024, "offset field is 12 bits");
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(tile + (wave * T::PER_WAVE + i) * 1024), 16,
-        lane_src, 0, 0, 0);
+        r,
+        (__attribute__((address_space(3))) void*)(tile + (wave * T::PER_WAVE + I) * 1024 - I * STEP),
+        16, lane_src, 0, I * STEP, 0);
+    dma_blocks<D, NW, STEP, I + 1>(r, tile, wave, lane_src);
   }
+}
+
+template <int D, int NW, int STEP>
+__device__ inline void dma_tile(uint8_t* tile, const uint16_t* head, uint32_t head_bytes, int key0,
+                                int wave, uint32_t lane_src) {
+  using T = DmaTile<D, NW>;
+  const uint32_t start = (uint32_t)key0 * T::RB;
+  // Scalar arithmetic (min then subtract) keeps the resource in SGPRs.
+  const uint32_t left = head_bytes - __builtin_amdgcn_readfirstlane(min(head_bytes, start));
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const uint8_t*>(head) + start, left);
+  dma_blocks<D, NW, STEP>(r, tile, wave, lane_src);
 }
 
 // Per-lane byte offsets of the matrix-core operand reads.
