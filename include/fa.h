@@ -77,8 +77,9 @@ enum {
  * Returns 0 for an invalid or empty problem. */
 size_t fa_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt);
 
-/* Bytes of device workspace fa_bwd needs: the float32 row terms
- * D_i = sum_c dO_ic O_ic and LSE_i log2(e), each [B, Hq, N_q], and, when there are too few key blocks
+/* Bytes of device workspace fa_bwd needs: the float32 row terms -D_i
+ * (D_i = sum_c dO_ic O_ic) and -LSE_i / scale, each [B, Hq, N_q], and, when
+ * there are too few key blocks
  * to fill the GPU (e.g. MQA), float32 partial dK and dV sums of the split
  * query-head groups. Linear in N ([KB] §06: storage O(N), not O(N^2)).
  * Returns 0 for an invalid or empty problem. */
@@ -109,7 +110,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
 /* One stage of fa_bwd, same arguments, for callers that interleave or time
  * the stages. Stages must run in order 0, 1, 2 on one workspace:
- *   0  D_i = sum_c dO_ic O_ic and LSE_i log2(e) into the workspace;
+ *   0  the row terms -D_i and -LSE_i / scale into the workspace;
  *   1  per key/value block: recompute P and dS over the query tiles that see
  *      it and write dk, dv (float32 partials into the workspace when the
  *      query-head group is split);
