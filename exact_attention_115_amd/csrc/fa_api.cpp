@@ -184,12 +184,13 @@ int run_bwd_stage(int stage, const Problem& p, const BwdPtrs& t, hipStream_t str
 }  // namespace
 
 DecodeSplit decode_split(const Problem& p) {
-  // Aim for about 1024 workgroups in flight over the key range, with at least
-  // 256 keys per split so each split streams a useful run of K/V.
-  const long long units = (long long)p.B * p.Hkv;
+  // One workgroup per CU (each keeps three 64-key tiles of K and V in
+  // flight): split the key range so that about 256 workgroups cover all
+  // (b, kv head, query-head group) units, with at least two tiles per split.
+  const long long units = (long long)p.B * p.Hkv * ((p.G + 31) / 32);
   const int tiles = (p.Nkv + 63) / 64;
-  long long want = (1024 + units - 1) / units;
-  long long max_splits = (p.Nkv + 255) / 256;
+  long long want = units > 0 ? (256 + units - 1) / units : 1;
+  long long max_splits = (tiles + 1) / 2;
   if (max_splits < 1) max_splits = 1;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;

@@ -33,22 +33,106 @@ struct DecArgs {
   float* part_o;    // [B*Hq][splits][D]
   float* part_lse;  // [B*Hq][splits]
   int Hq, Hkv, G, Nkv, splits, keys_per_split, n_qgroups;
+  uint32_t q_bytes;  // bytes of Q
   float scale_log2;
 };
 
-// One workgroup per (b, kv head, group of 32 query heads, split). All waves
-// compute the same 32-key x 32-head score tiles (cheap next to the stream of
-// K and V); wave w owns output dims [32w, 32w + 32).
-template <typename T, int D>
-__global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
-  using L = KVTileLds<D>;
-  using V8 = typename T::vec8;
-  constexpr int KC = D / 16;
+// Copy `blocks` 1 KiB blocks starting at byte `src` of a flat array (`bytes`
+// long; reads past the end fill zeros) to LDS at dst, block i of this wave
+// at dst + (wave * blocks + i) KiB, 16 bytes per lane. Issued from inline
+// assembly so that the compiler adds no waits of its own for them: the
+// caller waits on vmcnt before the barrier that precedes any read.
+__device__ __forceinline__ void copy_blocks_async(uint8_t* dst, const void* base, uint32_t bytes,
+                                                  uint32_t src, int wave, int lane, int blocks) {
+  for (int i = 0; i < blocks; ++i) {
+    const uint32_t start = src + (uint32_t)(wave * blocks + i) * 1024u;
+    const uint32_t left = bytes - __builtin_amdgcn_readfirstlane(min(bytes, start));
+    const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(base) + start);
+    u32x4 rsrc;  // base, stride 0, size, raw access with zero fill out of range
+    rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+    rsrc[2] = __builtin_amdgcn_readfirstlane(left);
+    rsrc[3] = 0x00020000u;
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t*)(dst + (wave * blocks + i) * 1024));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"((uint32_t)lane * 16u), "s"(rsrc)
+        : "memory", "m0");
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+// The same for one K or V tile in the blocked LDS layouts of fa_tile.h
+// (lane_src: k_dma_src or v_dma_src; step: K_STEP or V_STEP).
+template <int D>
+__device__ __forceinline__ void copy_tile_async(uint8_t* tile, const uint16_t* head,
+                                                uint32_t head_bytes, int key0, int wave,
+                                                uint32_t lane_src, int step) {
+  using DT = DmaTile<D, 4>;
+#pragma unroll
+  for (int i = 0; i < DT::PER_WAVE; ++i) {
+    const uint32_t start = (uint32_t)key0 * DT::RB + (uint32_t)(i * step);
+    const uint32_t left = head_bytes - __builtin_amdgcn_readfirstlane(min(head_bytes, start));
+    const uint64_t addr = reinterpret_cast<uint64_t>(reinterpret_cast<const uint8_t*>(head) + start);
+    u32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+    rsrc[2] = __builtin_amdgcn_readfirstlane(left);
+    rsrc[3] = 0x00020000u;
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t*)(tile + (wave * DT::PER_WAVE + i) * 1024));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds), "v"(lane_src), "s"(rsrc)
+        : "memory", "m0");
+  }
+}
+
+// Wait until at most N of this wave's copies are in flight and its LDS
+// reads have returned.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// One workgroup per (b, kv head, group of 32 query heads, split); the 32
+// heads are the matrix-core columns, so K and V are read once per group.
+// Each wave takes every fourth 64-key tile of the split and runs its own
+// online softmax over them ([KB] §04) in private LDS buffers: a K buffer
+// and a V buffer, each refilled with the wave's next tile as soon as its
+// products are issued, so a wave has a load in flight while it computes and
+// the waves need no barrier inside the loop. At the end the four partial
+// states are merged with the same rescaling rule and written as the split's
+// O_s = U / l and LSE_s.
+template <typename T, int D>
+__global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
+  using V8 = typename T::vec8;
+  using DT = DmaTile<D, 4>;
+  constexpr int KC = D / 16;
+  constexpr int OD = D / 32;
+  constexpr int TB = DT::BYTES;
+  constexpr int QB = 32 * DT::RB;        // the group's 32 query rows
+  constexpr int QBLK = QB / 1024 / 4;    // 1 KiB Q blocks per wave
+  constexpr int CPT = 4 * DT::PER_WAVE;  // copies per K (or V) tile, one wave
+  static_assert(QBLK >= 1, "Q blocks");
+  static_assert(4 * OD * 16 * 64 * 4 <= 4 * TB, "merge fits in the K buffers");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[4][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[4][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qbuf[QB];
+  __shared__ float mbuf[4][32], lbuf[4][32];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int c = lane & 31;
@@ -68,108 +152,159 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecArgs a) {
   const int key_end = min(a.Nkv, key_begin + a.keys_per_split);
   const int n_tiles = key_end > key_begin ? (key_end - key_begin + BC - 1) / BC : 0;
 
-  // Buffer resources over this split's keys: reads past key_end return zero.
+  // K / V of this split: reads past key_end fill zeros.
   const size_t split_off = ((size_t)bk * a.Nkv + key_begin) * D;
   const uint32_t split_bytes = (uint32_t)max(key_end - key_begin, 0) * D * 2u;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + split_off, split_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + split_off, split_bytes);
+  const uint16_t* khead = a.k + split_off;
+  const uint16_t* vhead = a.v + split_off;
+  uint8_t* const ks = kbuf[wave];
+  uint8_t* const vs = vbuf[wave];
+  // The whole tile by this wave: the four quarters the 4-wave copy layout
+  // assigns to waves 0..3.
+  auto load_k = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      copy_tile_async<D>(ks, khead, split_bytes, j * BC, w, k_dma_src<D, 4>(w, lane), DT::K_STEP);
+  };
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      copy_tile_async<D>(vs, vhead, split_bytes, j * BC, w, v_dma_src<D, 4>(w, lane), DT::V_STEP);
+  };
 
+  // The group's Q rows (rows past the group's heads are loaded but unused),
+  // copied by all waves; then each wave's first tile.
+  const size_t q_row0 = (size_t)b * a.Hq + hkv * a.G + qg * 32;
+  copy_blocks_async(qbuf, a.q, a.q_bytes, (uint32_t)(q_row0 * D * 2), wave, lane, QBLK);
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
+  load_k(wave);
+  load_v(wave);
+  wait_copies<2 * CPT>();  // this wave's Q blocks
+  __syncthreads();         // everyone's Q blocks
+
+  const uint32_t kr0 = k_read_base<D>(h, c, 0);
+  const uint32_t kr1 = k_read_base<D>(h, c, 1);
+  const uint32_t vr = v_read_base<D>(h, c);
   V8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
-    qf[kc] = as_vec8<T>(has_head ? ld16(a.q + row * D + kc * 16 + h * 8) : zero_u32x4());
+    qf[kc] = as_vec8<T>(*reinterpret_cast<const u32x4*>(qbuf + c * DT::RB + (16 * kc + 8 * h) * 2));
 
-  f32x16 oacc = zero16();
+  f32x16 oacc[OD];
+#pragma unroll
+  for (int od = 0; od < OD; ++od) oacc[od] = zero16();
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  const bool owns_dims = wave < D / 32;
 
-  KVTileRegs<D> regs;
-  if (n_tiles > 0) {
-    load_kv_tile<D>(regs, krs, vrs, 0, 0, tid);
-    store_kv_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
+  for (int n = 0; n < my_tiles; ++n) {
+    const int j = wave + 4 * n;  // tile of the split
+    const int key0 = key_begin + j * BC;
+    wait_copies<CPT>();  // K tile j (its V may still be in flight)
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint8_t* p = ks + ((kc & 1) ? kr1 : kr0) + kb * 32 * DT::RB + (kc >> 1) * 1024;
+        s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), qf[kc], s[kb]);
+      }
+    }
+    // The K buffer is free once its reads returned: refill it (tiles past
+    // the split fill zeros, so every pass issues the same copies).
+    wait_copies<CPT>();
+    load_k(j + 4);
+    if (key0 + BC > key_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb * 32 + acc_key(h, r) >= key_end) s[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * a.scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.0f;
+    uint32_t pk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7)], a.scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7) + 1], a.scale_log2, -m_use));
+      pk[i] = pack2<T>(p0, p1);
+      psum += p0 + p1;
+    }
+    l_run = fmaf(alpha, l_run, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int od = 0; od < OD; ++od)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
+    wait_copies<CPT>();  // V tile j (the K copies just issued may be in flight)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      u32x4 w;
+      w[0] = pk[4 * ch + 0];
+      w[1] = pk[4 * ch + 1];
+      w[2] = pk[4 * ch + 2];
+      w[3] = pk[4 * ch + 3];
+#pragma unroll
+      for (int od = 0; od < OD; ++od)
+        oacc[od] = T::mfma(load_vt_dma<T, D>(vs, vr, ch, od), as_vec8<T>(w), oacc[od]);
+    }
+    wait_copies<CPT>();
+    load_v(j + 4);
   }
+  // Copies past the split may still be in flight.
+  wait_copies<0>();
   __syncthreads();
 
-  int stage = 0;
-  for (int j = 0; j < n_tiles; ++j) {
-    const bool more = j + 1 < n_tiles;
-    const int key0 = key_begin + j * BC;
-    if (more) load_kv_tile<D>(regs, krs, vrs, (j + 1) * BC, (j + 1) * BC, tid);
-
-    const uint16_t* ks = smem + stage * L::STAGE;
-    const uint16_t* vt = ks + L::K_ELEMS;
-
-    if (owns_dims) {
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
-        const uint16_t* krow = ks + (kb * 32 + row_perm(c)) * L::RSK + h * 8;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(krow + kc * 16)), qf[kc], s[kb]);
-      }
-      if (key0 + BC > key_end) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + kb * 32 + acc_key(h, r) >= key_end) s[kb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.scale_log2, -m_use));
-          s[kb][r] = p;
-          psum += p;
-        }
-      l_run = fmaf(alpha, l_run, psum);
-      m_run = m_new;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[r] *= alpha;
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        float pv[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pv[t] = s[ch >> 1][(ch & 1) * 8 + t];
-        const V8 va = load_vt_operand<T, L::RSV>(vt, h, c, ch * 16, wave * 32);
-        oacc = T::mfma(va, pack8<T>(pv), oacc);
-      }
-    }
-
-    if (more) {
-      uint16_t* nks = smem + (stage ^ 1) * L::STAGE;
-      store_kv_tile<D>(regs, nks, nks + L::K_ELEMS, tid);
-    }
-    __syncthreads();
-    stage ^= 1;
+  // Merge the four waves' states: wave w leaves m, l and U in LDS (the K
+  // buffers), then wave v combines output dims [32v, 32v + 32).
+  const float l_tot = l_run + swap_halves(l_run);
+  if (h == 0) {
+    mbuf[wave][c] = m_run;
+    lbuf[wave][c] = l_tot;
   }
-
-  if (!owns_dims || !has_head) return;
-  const float l = l_run + swap_halves(l_run);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* ubuf = reinterpret_cast<float*>(&kbuf[0][0]);
+#pragma unroll
+  for (int od = 0; od < OD; ++od)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ubuf[((wave * OD + od) * 16 + r) * 64 + lane] = oacc[od][r];
+  __syncthreads();
+  if (wave >= OD || !has_head) return;
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = mbuf[w][c];
+    M = fmaxf(M, mw[w]);
+  }
+  const float M_use = (M == -INFINITY) ? 0.0f : M;
+  float L = 0.0f;
+  f32x16 u = zero16();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float f = __builtin_amdgcn_exp2f(mw[w] - M_use);
+    L = fmaf(f, lbuf[w][c], L);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) u[r] = fmaf(f, ubuf[((w * OD + wave) * 16 + r) * 64 + lane], u[r]);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float* po = a.part_o + (row * a.splits + split) * D + wave * 32;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     f32x4 out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = oacc[4 * g + i] * inv;
+    for (int i = 0; i < 4; ++i) out[i] = u[4 * g + i] * inv;
     *reinterpret_cast<f32x4*>(po + g * 8 + h * 4) = out;
   }
   if (wave == 0 && h == 0)
-    a.part_lse[row * a.splits + split] = l > 0.0f ? (m_run + __log2f(l)) * LN2 : -INFINITY;
+    a.part_lse[row * a.splits + split] = L > 0.0f ? (M + __log2f(L)) * LN2 : -INFINITY;
 }
 
 // Merge the splits of one (b, q head) row; one wave per row.
@@ -225,6 +360,7 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) 
   a.splits = sp.splits;
   a.keys_per_split = sp.keys_per_split;
   a.n_qgroups = (p.G + 31) / 32;
+  a.q_bytes = (uint32_t)((size_t)p.B * p.Hq * D * 2);
   a.scale_log2 = p.scale * LOG2E;
   dim3 grid((unsigned)((size_t)p.B * p.Hkv * a.n_qgroups * sp.splits));
   hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(NT), 0, stream, a);
