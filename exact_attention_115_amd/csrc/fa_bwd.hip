@@ -118,6 +118,32 @@ __device__ __forceinline__ void init_rows(const float* x, int h, f32x16* acc) {
       }
 }
 
+// Matrix-core products of the dK/dV kernel, issued from inline assembly so
+// that each accumulator stays in the register file its users need: the
+// scores and dP (read by the vector ALU) in vector registers with the
+// stationary K, V operand in accumulation registers (mfma_rows), dK and dV
+// (read once, at the end) in accumulation registers (mfma_acc). The
+// compiler places no hazard waits around these: results are read by other
+// instructions only after xdl_wait().
+template <typename T>
+__device__ __forceinline__ void mfma_rows(f32x16& c, typename T::vec8 a, typename T::vec8& b) {
+  // b is tied in and out so that it is used in place, not copied per product.
+  if constexpr (std::is_same_v<T, BF16>)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %1, %0" : "+v"(c), "+a"(b) : "v"(a));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %2, %1, %0" : "+v"(c), "+a"(b) : "v"(a));
+}
+template <typename T>
+__device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename T::vec8 b) {
+  if constexpr (std::is_same_v<T, BF16>)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 24 wait states: more than a 32x32x16 product needs before another
+// instruction may read its result.
+__device__ __forceinline__ void xdl_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // One step of the dK/dV pipeline for query tile i, as a single interleaved
 // instruction stream of three independent parts:
 //   * scores and dP of tile i + 1: sn = Q' K^T, dpn = dO' V^T (rows of the
@@ -136,7 +162,7 @@ __device__ __forceinline__ void init_rows(const float* x, int h, f32x16* acc) {
 template <typename T, int D, bool PREV>
 __device__ __forceinline__ void dkdv_step(
     const uint8_t* qn, const uint8_t* gn, const uint8_t* qp, const uint8_t* gp, uint32_t kr0,
-    uint32_t kr1, uint32_t kt0, uint32_t kt1, const typename T::vec8* kf, const typename T::vec8* vf,
+    uint32_t kr1, uint32_t kt0, uint32_t kt1, typename T::vec8* kf, typename T::vec8* vf,
     f32x16* sn, f32x16* dpn, f32x16* dk, f32x16* dv, const uint32_t* pp, const uint32_t* dsp,
     const f32x16* s, const f32x16* dpc, const float* ln, const float* dn, int h, float sl2,
     uint32_t* pc, uint32_t* dsc) {
@@ -175,9 +201,9 @@ __device__ __forceinline__ void dkdv_step(
       if (i + 2 < NR) rf[i + 2] = rfrag(i + 2);
       const int x = i & 1, qb = (i >> 1) & 1, kc = i >> 2;
       if (x)
-        dpn[qb] = T::mfma(as_vec8<T>(rf[i]), vf[kc], dpn[qb]);
+        mfma_rows<T>(dpn[qb], as_vec8<T>(rf[i]), vf[kc]);
       else
-        sn[qb] = T::mfma(as_vec8<T>(rf[i]), kf[kc], sn[qb]);
+        mfma_rows<T>(sn[qb], as_vec8<T>(rf[i]), kf[kc]);
     } else if constexpr (PREV) {
       if (i + 2 < NT) tf[i + 2] = tfrag(i + 2);
       const int y = i & 1, ch = (i >> 1) / OD, od = (i >> 1) % OD;
@@ -188,9 +214,9 @@ __device__ __forceinline__ void dkdv_step(
       w[2] = w4[2];
       w[3] = w4[3];
       if (y)
-        dk[od] = T::mfma(tf[i], as_vec8<T>(w), dk[od]);
+        mfma_acc<T>(dk[od], tf[i], as_vec8<T>(w));
       else
-        dv[od] = T::mfma(tf[i], as_vec8<T>(w), dv[od]);
+        mfma_acc<T>(dv[od], tf[i], as_vec8<T>(w));
     }
     // Tile i's P and dS: the 16 pairs in four parts each (fma + exp, the
     // rounding of P, the dS factors, the rounding of dS), spread evenly
@@ -234,8 +260,8 @@ __device__ __forceinline__ void dkdv_tail(const uint8_t* qp, const uint8_t* gp, 
     }
 #pragma unroll
     for (int od = 0; od < OD; ++od) {
-      dv[od] = T::mfma(load_kt_dma<T, D>(gp, kt0, kt1, ch, od), as_vec8<T>(wp), dv[od]);
-      dk[od] = T::mfma(load_kt_dma<T, D>(qp, kt0, kt1, ch, od), as_vec8<T>(ws), dk[od]);
+      mfma_acc<T>(dv[od], load_kt_dma<T, D>(gp, kt0, kt1, ch, od), as_vec8<T>(wp));
+      mfma_acc<T>(dk[od], load_kt_dma<T, D>(qp, kt0, kt1, ch, od), as_vec8<T>(ws));
     }
   }
 }
@@ -245,7 +271,7 @@ __device__ __forceinline__ void dkdv_tail(const uint8_t* qp, const uint8_t* gp, 
 // K-layout tile xs and the stationary B operand xf.
 template <typename T, int D>
 __device__ __forceinline__ void tile_rows(const uint8_t* xs, uint32_t kb0, uint32_t kb1,
-                                          const typename T::vec8* xf, const float* x0, int h,
+                                          typename T::vec8* xf, const float* x0, int h,
                                           f32x16* s) {
   constexpr int RB = DmaTile<D>::RB;
   constexpr int KC = D / 16;
@@ -255,7 +281,7 @@ __device__ __forceinline__ void tile_rows(const uint8_t* xs, uint32_t kb0, uint3
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const uint8_t* p = xs + ((kc & 1) ? kb1 : kb0) + qb * 32 * RB + (kc >> 1) * 1024;
-      s[qb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), xf[kc], s[qb]);
+      mfma_rows<T>(s[qb], as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), xf[kc]);
     }
   }
 }
@@ -414,6 +440,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     tile_rows<T, D>(qs0, kr0, kr1, kf, ls0, h, sa);
     tile_rows<T, D>(gs0, kr0, kr1, vf, ds0, h, da);
     load_tile(2, 2);
+    xdl_wait();
     mask_tile(0, sa);
     dkdv_step<T, D, false>(qs1, gs1, qs3, gs3, kr0, kr1, kt0, kt1, kf, vf, sb, db, dk, dv, pb, zb,
                            sa, da, ls1, ds1, h, sl2, pa, za);
@@ -434,6 +461,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
         load_tile(i + 2, (r + 3) & 3);
         f32x16* s = even ? sa : sb;
         f32x16* dpc = even ? da : db;
+        xdl_wait();  // the scores and dP of tile i were written last step
         mask_tile(i, s);
         dkdv_step<T, D, true>(qslot((r + 2) & 3), gslot((r + 2) & 3), qslot(r & 3), gslot(r & 3),
                               kr0, kr1, kt0, kt1, kf, vf, even ? sb : sa, even ? db : da, dk, dv,
@@ -449,6 +477,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const bool odd = (total - 1) & 1;
     dkdv_tail<T, D>(qslot(x), gslot(x), kt0, kt1, dk, dv, odd ? pb : pa, odd ? zb : za);
   }
+  xdl_wait();
 
   // ---- dK = scale * (sum dS^T Q) and dV (lane = key, 16 dims per tile); a
   // split head group writes float32 partial sums that stage 2 adds up.

@@ -240,7 +240,8 @@ hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
 template <typename T, int D>
 hipError_t launch_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
-  return big_tiles >= 256 ? launch_nw<T, D, 8>(p, t, stream) : launch_nw<T, D, 4>(p, t, stream);
+  return (big_tiles >= 256 && p.Nq >= 4096) ? launch_nw<T, D, 8>(p, t, stream)
+                                            : launch_nw<T, D, 4>(p, t, stream);
 }
 
 }  // namespace

@@ -415,11 +415,15 @@ hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// 256-row workgroups when they alone fill the 256 CUs, else 128-row ones.
+// 256-row workgroups when they alone fill the 256 CUs and the key range is
+// long (N_q >= 4096), else 128-row ones: on shorter sequences two workgroups
+// per CU overlap one's start-up with the other's main loop, which outweighs
+// sharing each K/V tile among 8 waves instead of 4.
 template <typename T, int D>
 hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
   const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
-  return big_tiles >= 256 ? launch_nw<T, D, 8>(p, t, stream) : launch_nw<T, D, 4>(p, t, stream);
+  return (big_tiles >= 256 && p.Nq >= 4096) ? launch_nw<T, D, 8>(p, t, stream)
+                                            : launch_nw<T, D, 4>(p, t, stream);
 }
 
 }  // namespace
