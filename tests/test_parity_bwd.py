@@ -61,6 +61,24 @@ def test_full_size_backward_sampled_heads(name):
         assert torch.isfinite(t).all()
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_ragged_backward_sampled_heads(causal):
+    """256-row dQ workgroups and many key blocks (N >= 4096), ragged last
+    tiles, causal and not."""
+    w = WORKLOADS["c3"].replace(name="long_ragged", Hq=16, Hkv=16, Nq=4100, Nkv=4100,
+                                causal=causal, seed=38)
+    say(f"{w}")
+    q, k, v, do = make_inputs(w)
+    _, (dq, dk, dv) = run_fwd_bwd(q, k, v, do, w.causal, w.scale)
+    heads_kv = [(0, w.Hkv - 1)]
+    refs = oracle_heads_backward(q, k, v, do, w.causal, w.scale, heads_kv)
+    for (b, hk), (dq_r, dk_r, dv_r) in zip(heads_kv, refs):
+        check_grads((dq[b, hk:hk + 1], dk[b, hk], dv[b, hk]), (dq_r, dk_r, dv_r), w.dtype,
+                    f"long ragged causal={causal}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
 EDGE = [
     # (B, Hq, Hkv, Nq, Nkv, d, causal)
     (1, 2, 2, 300, 300, 64, True),

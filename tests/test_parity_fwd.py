@@ -107,6 +107,23 @@ def test_full_size_forward_sampled_heads(name):
     assert torch.isfinite(o).all()
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_ragged_forward_sampled_heads(causal):
+    """256-row workgroups (N_q >= 4096 and enough of them to fill the GPU)
+    with a ragged last query and key tile, causal and not."""
+    w = WORKLOADS["c3"].replace(name="long_ragged", Hq=16, Hkv=16, Nq=4100, Nkv=4100,
+                                causal=causal, seed=37)
+    say(f"{w}")
+    q, k, v, _ = make_inputs(w, with_grad=False)
+    o, lse = run_forward(q, k, v, w.causal, w.scale)
+    heads = [(0, 0), (0, w.Hq - 1)]
+    o_ref, lse_ref = oracle_heads_forward(q, k, v, w.causal, w.scale, heads)
+    o_s = torch.stack([o[b, h] for b, h in heads])
+    l_s = torch.stack([lse[b, h] for b, h in heads])
+    check_forward(o_s, l_s, o_ref, lse_ref, w.dtype, f"long ragged causal={causal}")
+    assert torch.isfinite(o).all()
+
+
 @pytest.mark.parametrize("name", ["c5dg", "c5dm"])
 def test_decode_forward(name):
     w = WORKLOADS[name]
@@ -136,8 +153,8 @@ EDGE = [
     (3, 6, 3, 65, 129, 64, True),
     (1, 2, 1, 1, 1000, 128, True),     # decode, ragged split
     (2, 8, 2, 1, 64, 64, False),
-    (2, 64, 16, 1000, 1000, 128, True),  # 256-row workgroups, ragged last tile
-    (4, 32, 32, 700, 900, 64, False),    # 256-row workgroups, N_q < N_kv
+    (2, 64, 16, 1000, 1000, 128, True),  # many 128-row workgroups, ragged last tile
+    (4, 32, 32, 700, 900, 64, False),    # many workgroups, N_q < N_kv
 ]
 
 
