@@ -41,25 +41,6 @@ struct DqArgs {
   float scale, scale_log2;
 };
 
-// X^T from the K-layout tile at xs (xs: K or V), as in the forward's scores:
-// accumulator r of block kb holds key kb * 32 + acc_key(h, r) of this lane's
-// query row, for the B operand xf (Q or dO of the row).
-template <typename T, int D>
-__device__ __forceinline__ void row_products(const uint8_t* xs, uint32_t kb0, uint32_t kb1,
-                                             const typename T::vec8* xf, f32x16* s) {
-  constexpr int RB = DmaTile<D>::RB;
-  constexpr int KC = D / 16;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = zero16();
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const uint8_t* p = xs + ((kc & 1) ? kb1 : kb0) + kb * 32 * RB + (kc >> 1) * 1024;
-      s[kb] = T::mfma(as_vec8<T>(*reinterpret_cast<const u32x4*>(p)), xf[kc], s[kb]);
-    }
-  }
-}
-
 // NW waves of 32 query rows per workgroup (8 when the grid fills the GPU,
 // else 4), as in the forward.
 template <typename T, int D, bool CAUSAL, int NW>
@@ -140,10 +121,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
 #pragma unroll
   for (int od = 0; od < OD; ++od) acc[od] = zero16();
 
+  // One key tile, as one instruction stream of 48 products with the vector
+  // work spread over the last 32 (scheduling fences keep the order):
+  //   S = K Q^T (16 products), then the mask on tiles that need it;
+  //   dP = V dO^T (16): each followed by the exponentials of one pair of
+  //     scores, P = exp2(S scale_log2 - LSE) kept in float32 in place of S;
+  //   dQ^T += K^T dS^T (16, four per 16-key chunk ch): dS = P (dP - D)
+  //     of the pairs of chunk ch, rounded to 16 bits, is formed while the
+  //     products of chunk ch - 1 run (chunk 0's during the last dP products).
+  // LDS operands are read two products ahead.
   auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
+    constexpr int RB = DT::RB;
     f32x16 s[2], dp[2];
-    row_products<T, D>(kt, kr0, kr1, qf, s);
-    row_products<T, D>(vt, kr0, kr1, gf, dp);
+    auto rfrag = [&](const uint8_t* xs, int q) {
+      const int kb = q / KC, kc = q % KC;
+      return *reinterpret_cast<const u32x4*>(xs + ((kc & 1) ? kr1 : kr0) + kb * 32 * RB +
+                                             (kc >> 1) * 1024);
+    };
+    constexpr int NR = 2 * KC;  // products per score block pair (S or dP)
+    u32x4 rf[NR];
+    s[0] = zero16();
+    s[1] = zero16();
+    rf[0] = rfrag(kt, 0);
+    rf[1] = rfrag(kt, 1);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      if (q + 2 < NR) rf[q + 2] = rfrag(kt, q + 2);
+      s[q / KC] = T::mfma(as_vec8<T>(rf[q]), qf[q % KC], s[q / KC]);
+    }
     const int key0 = j * BC;
     if ((key0 + BC > Nkv) || (CAUSAL && key0 + BC - 1 > q0 + offset)) {
       const int lim = CAUSAL ? min(Nkv - 1, qrow + offset) : Nkv - 1;
@@ -153,27 +158,59 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
         for (int r = 0; r < 16; ++r)
           if (key0 + kb * 32 + acc_key(h, r) > lim) s[kb][r] = -INFINITY;
     }
-    // dS = P (dP - D), rounded to 16 bits: ds[4 ch + t] holds the keys
-    // 16 ch + 8 h + 2t, +1 (the B operand of chunk ch of dQ^T += K^T dS^T).
+    // ds[4 ch + t] holds dS of keys 16 ch + 8 h + 2t, +1 (the B operand of
+    // chunk ch of dQ^T += K^T dS^T); pair e of the scores is accumulators
+    // 2 (e % 8), +1 of block e / 8.
     uint32_t ds[16];
+    auto exp_pair = [&](int e) __attribute__((always_inline)) {
+      const int kb = e >> 3, r = 2 * (e & 7);
+      s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -lse2));
+      s[kb][r + 1] = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -lse2));
+    };
+    auto ds_pair = [&](int e) __attribute__((always_inline)) {
+      const int kb = e >> 3, r = 2 * (e & 7);
+      ds[e] = pack2<T>(s[kb][r] * (dp[kb][r] + ndrow), s[kb][r + 1] * (dp[kb][r + 1] + ndrow));
+    };
+    dp[0] = zero16();
+    dp[1] = zero16();
+    rf[0] = rfrag(vt, 0);
+    rf[1] = rfrag(vt, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kb = i >> 3, r = 2 * (i & 7);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -lse2));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], sl2, -lse2));
-      ds[i] = pack2<T>(p0 * (dp[kb][r] + ndrow), p1 * (dp[kb][r + 1] + ndrow));
+    for (int q = 0; q < NR; ++q) {
+      if (q + 2 < NR) rf[q + 2] = rfrag(vt, q + 2);
+      dp[q / KC] = T::mfma(as_vec8<T>(rf[q]), gf[q % KC], dp[q / KC]);
+      // 16 pairs of exponentials over the NR products, then the dS of
+      // chunk 0 (block 0's dP is complete once half the products ran).
+#pragma unroll
+      for (int e = q * 16 / NR; e < (q + 1) * 16 / NR; ++e) exp_pair(e);
+      if (q >= NR / 2 + NR / 4) {
+#pragma unroll
+        for (int e = (q - NR / 2 - NR / 4) * 4 / (NR / 4); e < (q + 1 - NR / 2 - NR / 4) * 4 / (NR / 4);
+             ++e)
+          ds_pair(e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    V8 tf[4 * OD];
+    tf[0] = load_kt_dma<T, D>(kt, kt0, kt1, 0, 0);
+    tf[1] = load_kt_dma<T, D>(kt, kt0, kt1, 0, 1 % OD);
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int t = 0; t < 4 * OD; ++t) {
+      const int ch = t / OD, od = t % OD;
+      if (t + 2 < 4 * OD) tf[t + 2] = load_kt_dma<T, D>(kt, kt0, kt1, (t + 2) / OD, (t + 2) % OD);
       u32x4 w;
       w[0] = ds[4 * ch + 0];
       w[1] = ds[4 * ch + 1];
       w[2] = ds[4 * ch + 2];
       w[3] = ds[4 * ch + 3];
-      const V8 bf = as_vec8<T>(w);
+      acc[od] = T::mfma(tf[t], as_vec8<T>(w), acc[od]);
+      // dS of chunk ch + 1 while chunk ch's products run.
+      if (ch + 1 < 4) {
 #pragma unroll
-      for (int od = 0; od < OD; ++od)
-        acc[od] = T::mfma(load_kt_dma<T, D>(kt, kt0, kt1, ch, od), bf, acc[od]);
+        for (int e = 4 * (ch + 1) + od * 4 / OD; e < 4 * (ch + 1) + (od + 1) * 4 / OD; ++e) ds_pair(e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
