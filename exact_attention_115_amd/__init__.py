@@ -3,7 +3,8 @@ split-KV decode in hand-written HIP kernels behind a C ABI (include/fa.h).
 
 Python names mirror the C entry points (``fa_fwd``, ``fa_bwd``,
 ``fa_bwd_stage``, ``fa_fwd_workspace_size``, ``fa_bwd_workspace_size``,
-``fa_strerror``, ``fa_version``); ``forward`` and ``backward`` allocate the
+``fa_fwd_paged``, ``fa_fwd_paged_workspace_size``, ``fa_strerror``,
+``fa_version``); ``forward``, ``backward`` and ``forward_paged`` allocate the
 outputs and the workspace and raise on error.
 """
 
@@ -19,9 +20,12 @@ from ._lib import (  # noqa: F401
     fa_bwd_stage,
     fa_bwd_workspace_size,
     fa_fwd,
+    fa_fwd_paged,
+    fa_fwd_paged_workspace_size,
     fa_fwd_workspace_size,
     fa_strerror,
     fa_version,
     forward,
+    forward_paged,
     load,
 )

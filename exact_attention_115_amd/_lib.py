@@ -64,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
+    lib.fa_fwd_paged_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_fwd_paged_workspace_size.restype = sz
+    lib.fa_fwd_paged.argtypes = [vp] * 8 + [sz] + [i] * 7 + [f, i, vp]
+    lib.fa_fwd_paged.restype = i
     _lib = lib
     return lib
 
@@ -190,3 +194,55 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_fwd_paged_workspace_size(B, Hq, Hkv, page_size, max_pages, d, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(load().fa_fwd_paged_workspace_size(B, Hq, Hkv, page_size, max_pages, d, code))
+
+
+def _paged_dims(q, k_pages, page_table):
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [batch, heads, 1, head_dim]")
+    if k_pages.dim() != 4:
+        raise ValueError("k_pages, v_pages must be [num_pages, kv_heads, page_size, head_dim]")
+    if page_table.dim() != 2 or page_table.shape[0] != q.shape[0]:
+        raise ValueError("page_table must be [batch, max_pages]")
+    B, Hq, _, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pages.shape
+    if dk != d:
+        raise ValueError(f"head_dim mismatch q {tuple(q.shape)} vs k_pages {tuple(k_pages.shape)}")
+    return B, Hq, Hkv, num_pages, page_size, page_table.shape[1], d
+
+
+def fa_fwd_paged(q, k_pages, v_pages, page_table, seq_lens, o, lse, workspace, scale: float,
+                 stream=None) -> int:
+    """Call fa_fwd_paged on tensors; returns the status code (no exception)."""
+    _check({"q": q, "k_pages": k_pages, "v_pages": v_pages, "o": o}, q.dtype)
+    _check({"page_table": page_table, "seq_lens": seq_lens}, torch.int32)
+    _check({"lse": lse}, torch.float32)
+    _check({"workspace": workspace})
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must have the same shape")
+    B, Hq, Hkv, num_pages, page_size, max_pages, d = _paged_dims(q, k_pages, page_table)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load().fa_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
+                               _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, B, Hq,
+                               Hkv, num_pages, page_size, max_pages, d, float(scale),
+                               _dtype_code(q), _stream(stream))
+
+
+def forward_paged(q, k_pages, v_pages, page_table, seq_lens, scale: float | None = None,
+                  stream=None):
+    """Decode over a paged K/V cache: O [B, Hq, 1, d], LSE [B, Hq, 1].
+    Allocates o, lse and the workspace."""
+    B, Hq, Hkv, num_pages, page_size, max_pages, d = _paged_dims(q, k_pages, page_table)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device)
+    ws = _workspace(fa_fwd_paged_workspace_size(B, Hq, Hkv, page_size, max_pages, d, q.dtype),
+                    q.device)
+    st = fa_fwd_paged(q, k_pages, v_pages, page_table, seq_lens, o, lse, ws,
+                      _default_scale(d, scale), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_paged")
+    return o, lse

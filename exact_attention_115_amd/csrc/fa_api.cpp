@@ -234,6 +234,59 @@ size_t bwd_workspace_bytes(const Problem& p) {
 
 using namespace fa;
 
+// Paged decode: the shape of the equivalent contiguous decode (N_q = 1,
+// N_kv = max_pages * page_size) plus the page geometry.
+static int check_paged_shape(int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                      int dt, bool* empty) {
+  if (num_pages < 0 || page_size < 0 || max_pages < 0) return FA_ERR_SHAPE;
+  if (dt != FA_F16 && dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (page_size == 0 || page_size % 64 != 0) return FA_ERR_UNSUPPORTED;
+  if (max_pages == 0 || num_pages == 0) return FA_ERR_SHAPE;
+  const long long nkv = (long long)max_pages * page_size;
+  if (nkv >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  int st = check_shape(B, Hq, Hkv, 1, (int)nkv, d, dt, empty);
+  if (st != FA_OK) return st;
+  // One page of one kv head is addressed with 32-bit byte offsets; pages with
+  // 64-bit ones.
+  if ((long long)num_pages * Hkv * page_size >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+static int check_paged(const void* q, const void* kp, const void* vp, const int* table, const int* lens,
+                void* o, float* lse, void* ws, size_t ws_bytes, int B, int Hq, int Hkv,
+                int num_pages, int page_size, int max_pages, int d, float scale, int dt,
+                bool* empty, Problem* prob) {
+  int st = check_paged_shape(B, Hq, Hkv, num_pages, page_size, max_pages, d, dt, empty);
+  if (st != FA_OK) return st;
+  st = check_scale(scale, 0);
+  if (st != FA_OK) return st;
+  if (*empty) return FA_OK;
+  *prob = make_problem(B, Hq, Hkv, 1, max_pages * page_size, d, scale, 0, (fa_dtype)dt);
+  const size_t e = elem_bytes((fa_dtype)dt);
+  const size_t qb = (size_t)B * Hq * d * e;
+  const size_t pb = (size_t)num_pages * Hkv * page_size * d * e;
+  const size_t tb = (size_t)B * max_pages * sizeof(int);
+  const size_t nb = (size_t)B * sizeof(int);
+  const size_t lb = (size_t)B * Hq * sizeof(float);
+  if (!q || !kp || !vp || !table || !lens || !o || !lse || !ws) return FA_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(kp, 16) || !aligned(vp, 16) || !aligned(o, 16) ||
+      !aligned(lse, 16) || !aligned(table, 4) || !aligned(lens, 4))
+    return FA_ERR_ALIGNMENT;
+  const size_t need = decode_workspace_bytes(*prob);
+  if (!aligned(ws, 256)) return FA_ERR_ALIGNMENT;
+  if (ws_bytes < need) return FA_ERR_WORKSPACE;
+  const Range in[5] = {range_of(q, qb), range_of(kp, pb), range_of(vp, pb), range_of(table, tb),
+                       range_of(lens, nb)};
+  const Range out[3] = {range_of(o, qb), range_of(lse, lb), range_of(ws, need)};
+  for (const Range& a : out) {
+    for (const Range& b : in)
+      if (overlap(a, b)) return FA_ERR_OVERLAP;
+  }
+  if (overlap(out[0], out[1]) || overlap(out[0], out[2]) || overlap(out[1], out[2]))
+    return FA_ERR_OVERLAP;
+  return FA_OK;
+}
+
 extern "C" {
 
 size_t fa_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt) {
@@ -293,6 +346,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     if (st != FA_OK) return st;
   }
   return FA_OK;
+}
+
+size_t fa_fwd_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
+                                   fa_dtype dt) {
+  bool empty = false;
+  if (check_paged_shape(B, Hq, Hkv, 1, page_size, max_pages, d, dt, &empty) != FA_OK || empty)
+    return 0;
+  Problem p = make_problem(B, Hq, Hkv, 1, max_pages * page_size, d, 1.0f, 0, dt);
+  return decode_workspace_bytes(p);
+}
+
+int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages, const int* page_table,
+                 const int* seq_lens, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, int B, int Hq, int Hkv, int num_pages, int page_size,
+                 int max_pages, int d, float scale, fa_dtype dt, hipStream_t stream) {
+  bool empty = false;
+  Problem p;
+  int st = check_paged(q, k_pages, v_pages, page_table, seq_lens, o, lse, workspace,
+                       workspace_bytes, B, Hq, Hkv, num_pages, page_size, max_pages, d, scale, dt,
+                       &empty, &p);
+  if (st != FA_OK || empty) return st;
+  FwdPtrs t{q, k_pages, v_pages, o, lse, workspace};
+  PagedPtrs pg{page_table, seq_lens, page_size, max_pages, num_pages};
+  return to_status(launch_decode_paged(p, t, pg, stream));
 }
 
 const char* fa_strerror(int status) {

@@ -28,13 +28,18 @@ constexpr float LOG2E = 1.44269504088896340736f;
 
 struct DecArgs {
   const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* k;   // [B, Hkv, Nkv, D], or the K page pool [num_pages, Hkv, page_size, D]
+  const uint16_t* v;   // likewise
   float* part_o;    // [B*Hq][splits][D]
   float* part_lse;  // [B*Hq][splits]
   int Hq, Hkv, G, Nkv, splits, keys_per_split, n_qgroups;
   uint32_t q_bytes;  // bytes of Q
   float scale_log2;
+  // Paged K/V: page_table [B, max_pages] (physical page of each logical
+  // page), seq_lens [B]; Nkv = max_pages * page_size.
+  const int* page_table;
+  const int* seq_lens;
+  int page_size, max_pages, num_pages;
 };
 
 // Copy `blocks` 1 KiB blocks starting at byte `src` of a flat array (`bytes`
@@ -113,7 +118,7 @@ __device__ __forceinline__ void wait_copies() {
 // the waves need no barrier inside the loop. At the end the four partial
 // states are merged with the same rescaling rule and written as the split's
 // O_s = U / l and LSE_s.
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
   using V8 = typename T::vec8;
   using DT = DmaTile<D, 4>;
@@ -148,28 +153,64 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
   const int hq = hkv * a.G + gi;
   const size_t row = (size_t)b * a.Hq + hq;  // (b, hq) row of Q, O, LSE
 
+  // Keys of this sequence (paged: its own length, read as a scalar).
+  int n_keys = a.Nkv;
+  if constexpr (PAGED) {
+    const auto* lens = (const __attribute__((address_space(4))) int*)a.seq_lens;
+    n_keys = min(max(lens[b], 0), a.Nkv);
+  }
   const int key_begin = split * a.keys_per_split;
-  const int key_end = min(a.Nkv, key_begin + a.keys_per_split);
+  const int key_end = min(n_keys, key_begin + a.keys_per_split);
   const int n_tiles = key_end > key_begin ? (key_end - key_begin + BC - 1) / BC : 0;
 
-  // K / V of this split: reads past key_end fill zeros.
-  const size_t split_off = ((size_t)bk * a.Nkv + key_begin) * D;
-  const uint32_t split_bytes = (uint32_t)max(key_end - key_begin, 0) * D * 2u;
-  const uint16_t* khead = a.k + split_off;
-  const uint16_t* vhead = a.v + split_off;
+  // Where tile j of the split comes from: a base pointer, the bytes that may
+  // be read from it (reads past them fill zeros) and the tile's first key
+  // relative to the base. Contiguous: the split's range. Paged: the tile's
+  // page (a page holds a whole number of 64-key tiles); a table entry out of
+  // [0, num_pages) reads as a page of zeros.
+  struct Src {
+    const uint16_t* k;
+    const uint16_t* v;
+    uint32_t bytes;
+    int key0;
+  };
+  auto tile_src = [&](int j) __attribute__((always_inline)) -> Src {
+    Src r;
+    if constexpr (!PAGED) {
+      const size_t split_off = ((size_t)bk * a.Nkv + key_begin) * D;
+      r.k = a.k + split_off;
+      r.v = a.v + split_off;
+      r.bytes = (uint32_t)max(key_end - key_begin, 0) * D * 2u;
+      r.key0 = j * BC;
+    } else {
+      const int key0 = key_begin + j * BC;  // key of the sequence
+      const int pg = __builtin_amdgcn_readfirstlane(min(key0 / a.page_size, a.max_pages - 1));
+      const auto* table = (const __attribute__((address_space(4))) int*)a.page_table;
+      const int phys = table[(size_t)b * a.max_pages + pg];
+      const bool ok = phys >= 0 && phys < a.num_pages && key0 < key_end;
+      const size_t off = (((size_t)(ok ? phys : 0) * a.Hkv + hkv) * a.page_size + key0 % a.page_size) * D;
+      r.k = a.k + off;
+      r.v = a.v + off;
+      r.bytes = ok ? (uint32_t)min(key_end - key0, BC) * D * 2u : 0u;
+      r.key0 = 0;
+    }
+    return r;
+  };
   uint8_t* const ks = kbuf[wave];
   uint8_t* const vs = vbuf[wave];
   // The whole tile by this wave: the four quarters the 4-wave copy layout
   // assigns to waves 0..3.
   auto load_k = [&](int j) __attribute__((always_inline)) {
+    const Src t = tile_src(j);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      copy_tile_async<D>(ks, khead, split_bytes, j * BC, w, k_dma_src<D, 4>(w, lane), DT::K_STEP);
+      copy_tile_async<D>(ks, t.k, t.bytes, t.key0, w, k_dma_src<D, 4>(w, lane), DT::K_STEP);
   };
   auto load_v = [&](int j) __attribute__((always_inline)) {
+    const Src t = tile_src(j);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      copy_tile_async<D>(vs, vhead, split_bytes, j * BC, w, v_dma_src<D, 4>(w, lane), DT::V_STEP);
+      copy_tile_async<D>(vs, t.v, t.bytes, t.key0, w, v_dma_src<D, 4>(w, lane), DT::V_STEP);
   };
 
   // The group's Q rows (rows past the group's heads are loaded but unused),
@@ -342,8 +383,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-template <typename T, int D>
-hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+template <typename T, int D, bool PAGED>
+hipError_t launch_typed(const Problem& p, const FwdPtrs& t, const PagedPtrs* pg,
+                        hipStream_t stream) {
   const DecodeSplit sp = decode_split(p);
   const size_t rows = (size_t)p.B * p.Hq;
   DecArgs a;
@@ -362,8 +404,13 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) 
   a.n_qgroups = (p.G + 31) / 32;
   a.q_bytes = (uint32_t)((size_t)p.B * p.Hq * D * 2);
   a.scale_log2 = p.scale * LOG2E;
+  a.page_table = PAGED ? pg->page_table : nullptr;
+  a.seq_lens = PAGED ? pg->seq_lens : nullptr;
+  a.page_size = PAGED ? pg->page_size : 0;
+  a.max_pages = PAGED ? pg->max_pages : 0;
+  a.num_pages = PAGED ? pg->num_pages : 0;
   dim3 grid((unsigned)((size_t)p.B * p.Hkv * a.n_qgroups * sp.splits));
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, PAGED>), grid, dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 cgrid((unsigned)((rows + 3) / 4));
@@ -376,8 +423,19 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) 
 
 hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
   if (p.dt == FA_BF16)
-    return p.d == 64 ? launch_typed<BF16, 64>(p, t, stream) : launch_typed<BF16, 128>(p, t, stream);
-  return p.d == 64 ? launch_typed<F16, 64>(p, t, stream) : launch_typed<F16, 128>(p, t, stream);
+    return p.d == 64 ? launch_typed<BF16, 64, false>(p, t, nullptr, stream)
+                     : launch_typed<BF16, 128, false>(p, t, nullptr, stream);
+  return p.d == 64 ? launch_typed<F16, 64, false>(p, t, nullptr, stream)
+                   : launch_typed<F16, 128, false>(p, t, nullptr, stream);
+}
+
+hipError_t launch_decode_paged(const Problem& p, const FwdPtrs& t, const PagedPtrs& pg,
+                               hipStream_t stream) {
+  if (p.dt == FA_BF16)
+    return p.d == 64 ? launch_typed<BF16, 64, true>(p, t, &pg, stream)
+                     : launch_typed<BF16, 128, true>(p, t, &pg, stream);
+  return p.d == 64 ? launch_typed<F16, 64, true>(p, t, &pg, stream)
+                   : launch_typed<F16, 128, true>(p, t, &pg, stream);
 }
 
 }  // namespace fa

@@ -27,6 +27,15 @@ struct FwdPtrs {
   void* ws;          // decode split state, else unused
 };
 
+// Paged K/V for decode: the page pools take the places of k and v in
+// FwdPtrs ([num_pages, Hkv, page_size, d]); Problem::Nkv = max_pages *
+// page_size.
+struct PagedPtrs {
+  const int* page_table;  // [B, max_pages] physical page of each logical page
+  const int* seq_lens;    // [B] keys of each sequence
+  int page_size, max_pages, num_pages;
+};
+
 struct BwdPtrs {
   const void* q;
   const void* k;
@@ -62,6 +71,8 @@ int bwd_group_split(const Problem& p);
 hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream);
 hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream);
 hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+hipError_t launch_decode_paged(const Problem& p, const FwdPtrs& t, const PagedPtrs& pg,
+                               hipStream_t stream);
 hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 hipError_t launch_bwd_dq(const Problem& p, const BwdPtrs& t, hipStream_t stream);

@@ -124,6 +124,37 @@ int fa_bwd_stage(int stage,
                  int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                  float scale, int causal, fa_dtype dt, hipStream_t stream);
 
+/* Decode (one query row per sequence) over a paged K/V cache ([KB]
+ * "FlashAttention：为什么少搬数据，反而算得更快" §09 names paged KV as the
+ * decode-side neighbour of FlashAttention; this is the same split-KV decode as
+ * fa_fwd with N_q == 1, its K/V gathered through a page table):
+ *   q          [B, Hq, 1, d], dtype dt (FA_F16 or FA_BF16)
+ *   k_pages,   [num_pages, Hkv, page_size, d] page pools, dtype dt: page n
+ *   v_pages    holds, for every kv head, page_size consecutive keys
+ *   page_table int32 [B, max_pages], device memory: entry p of row b is the
+ *              pool page that holds keys p*page_size .. (p+1)*page_size - 1
+ *              of sequence b
+ *   seq_lens   int32 [B], device memory: keys of sequence b (the query row
+ *              sees all of them; causal masking has no effect with one row)
+ *   o          [B, Hq, 1, d], dtype dt;  lse [B, Hq] float32
+ * page_size must be a positive multiple of 64. Values in device memory are
+ * not checked on the host: a table entry outside [0, num_pages) reads as a
+ * page of zeros, and lengths are clamped to [0, max_pages * page_size]; a
+ * sequence of length 0 gets o = 0, lse = -inf. Entries past a sequence's
+ * pages are not read. The workspace (fa_fwd_paged_workspace_size) holds the
+ * float32 partial results of the key-range splits; 256-byte aligned. Same
+ * status codes and aliasing rules as fa_fwd; asynchronous on stream. */
+int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
+                 const int* page_table, const int* seq_lens, void* o, float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                 float scale, fa_dtype dt, hipStream_t stream);
+
+/* Bytes of device workspace fa_fwd_paged needs (0 for an invalid or empty
+ * problem). */
+size_t fa_fwd_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
+                                   fa_dtype dt);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -32,6 +32,9 @@ Modules
 ``brute``      scalar pure-Python loops for tiny inputs (a second, independent
                spelling of the definition).
 
+``reference.paged_decode_forward`` is decode over a paged K/V cache: the keys
+of each sequence gathered through its page-table row, then the definition.
+
 Readings of the pages where they are silent are listed in ``reference``.
 Parity status: every function here is pinned by a CPU test in
 ``tests/test_oracle.py``; the only unpinned convention is the output of a
@@ -44,6 +47,8 @@ from .reference import (  # noqa: F401
     attention_backward,
     head_forward,
     head_backward,
+    paged_decode_forward,
+    paged_gather,
     visible_mask,
 )
 from .online import online_row, online_forward  # noqa: F401

@@ -164,3 +164,38 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
             dk[b, h // G] += kg
             dv[b, h // G] += vg
     return dq, dk, dv
+
+
+def paged_gather(pool, page_table_row, n_keys: int):
+    """The first n_keys keys of one sequence from a page pool
+    [num_pages, Hkv, page_size, d] and its row of the page table: logical page
+    p (keys p*page_size ..) lives in pool page page_table_row[p]. Returns
+    [Hkv, n_keys, d]."""
+    page_size = pool.shape[2]
+    n_pages = -(-n_keys // page_size)
+    pages = [pool[int(page_table_row[p])] for p in range(n_pages)]
+    if not pages:
+        return np.zeros((pool.shape[1], 0, pool.shape[3]))
+    return np.concatenate(pages, axis=1)[:, :n_keys]
+
+
+def paged_decode_forward(q, k_pages, v_pages, page_table, seq_lens, scale: float):
+    """Decode over a paged K/V cache ([KB] §09 pairs paged KV with decode):
+    q [B, Hq, 1, d]; k_pages, v_pages [num_pages, Hkv, page_size, d];
+    page_table [B, max_pages]; seq_lens [B]. Each sequence's K and V are
+    gathered through its table row and the single query row attends to all of
+    them (no mask). Returns (O [B, Hq, 1, d], LSE [B, Hq, 1])."""
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, 1, v_pages.shape[3]))
+    lse = np.full((B, Hq, 1), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        kb = paged_gather(k_pages, page_table[b], n)
+        vb = paged_gather(v_pages, page_table[b], n)
+        for h in range(Hq):
+            o[b, h], lse[b, h] = head_forward(q[b, h], kb[h // G], vb[h // G], False, scale)
+    return o, lse

@@ -147,3 +147,42 @@ def test_bwd_rejects_bad_arguments():
     assert bwd(stage=3) == -3
     assert bwd(stage=-1) == -3
     assert bwd(B=0) == 0
+
+
+def paged(q=P(1), kp=P(2), vp=P(3), table=P(4), lens=P(5), o=P(6), lse=P(7), ws=P(8),
+          ws_bytes=1 << 30, B=2, Hq=4, Hkv=2, num_pages=8, page_size=64, max_pages=4, d=64,
+          scale=0.125, dt=fa.FA_BF16):
+    return fa.load().fa_fwd_paged(q, kp, vp, table, lens, o, lse, ws, ws_bytes, B, Hq, Hkv,
+                                  num_pages, page_size, max_pages, d, scale, dt, None)
+
+
+def test_paged_workspace_matches_contiguous_decode():
+    lib = fa.load()
+    for B, Hq, Hkv, ps, mp, d in [(16, 32, 8, 128, 64, 128), (3, 8, 2, 64, 20, 64), (2, 32, 1, 256, 8, 128)]:
+        want = lib.fa_fwd_workspace_size(B, Hq, Hkv, 1, ps * mp, d, fa.FA_BF16)
+        assert lib.fa_fwd_paged_workspace_size(B, Hq, Hkv, ps, mp, d, fa.FA_BF16) == want > 0
+    assert lib.fa_fwd_paged_workspace_size(2, 4, 2, 96, 4, 64, fa.FA_BF16) == 0   # page size
+    assert lib.fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_F32) == 0    # dtype
+
+
+def test_paged_rejects_bad_arguments():
+    assert paged(page_size=96) == -3          # not a multiple of 64
+    assert paged(page_size=0) == -3
+    assert paged(dt=fa.FA_F32) == -3
+    assert paged(d=96) == -3
+    assert paged(max_pages=0) == -2
+    assert paged(num_pages=0) == -2
+    assert paged(Hq=3) == -2
+    assert paged(page_size=-64) == -2
+    assert paged(table=None) == -1
+    assert paged(lens=None) == -1
+    assert paged(ws=None) == -1
+    assert paged(lens=P(5, 2)) == -4          # int32 array not 4-byte aligned
+    assert paged(q=P(1, 8)) == -4
+    assert paged(ws=P(8, 16)) == -4
+    need = fa.load().fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_BF16)
+    assert paged(ws_bytes=need - 1) == -5
+    assert paged(scale=0.0) == -6
+    assert paged(o=P(1)) == -8                # output aliases q
+    assert paged(ws=P(4)) == -8               # workspace aliases the page table
+    assert paged(B=0) == 0                    # nothing to do

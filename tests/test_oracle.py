@@ -300,3 +300,44 @@ def test_planted_softmax_without_max_is_harmless_but_wrong_sum_is_caught(monkeyp
     n = _catches(monkeypatch, "_softmax_rows", wrong,
                  [test_hand_example_one_block, lambda: test_rows_sum_to_one(False, 9, 9)])
     assert n >= 1
+
+
+@pytest.mark.parametrize("page_size", [64, 128])
+def test_paged_decode_equals_contiguous_decode(page_size):
+    """Paged decode oracle against the definition on contiguous K/V: keys of
+    each sequence scattered into a shuffled page pool must give the same
+    O and LSE as the plain forward over that sequence's first len keys (the
+    contiguous side slices the original arrays directly, not through the
+    paging code)."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, d = 3, 4, 2, 64
+    lens = [1, 3 * page_size + 5, 2 * page_size]
+    max_pages = 4
+    n = max_pages * page_size
+    k = rng.standard_normal((B, Hkv, n, d))
+    v = rng.standard_normal((B, Hkv, n, d))
+    q = rng.standard_normal((B, Hq, 1, d))
+    num_pages = B * max_pages + 2
+    order = rng.permutation(num_pages)
+    table = order[: B * max_pages].reshape(B, max_pages)
+    k_pages = rng.standard_normal((num_pages, Hkv, page_size, d))  # unused pages: noise
+    v_pages = rng.standard_normal((num_pages, Hkv, page_size, d))
+    for b in range(B):
+        for p in range(max_pages):
+            k_pages[table[b, p]] = k[b, :, p * page_size:(p + 1) * page_size]
+            v_pages[table[b, p]] = v[b, :, p * page_size:(p + 1) * page_size]
+    o, lse = oracle.paged_decode_forward(q, k_pages, v_pages, table, np.array(lens), 0.125)
+    for b in range(B):
+        ob, lb = oracle.attention_forward(q[b:b + 1], k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]],
+                                          False, 0.125)
+        np.testing.assert_allclose(o[b], ob[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], lb[0], rtol=0, atol=1e-12)
+
+
+def test_paged_decode_empty_sequence():
+    """A sequence with no keys: O = 0, LSE = -inf (the no-key convention)."""
+    rng = np.random.default_rng(8)
+    k_pages = rng.standard_normal((2, 1, 64, 64))
+    q = rng.standard_normal((1, 2, 1, 64))
+    o, lse = oracle.paged_decode_forward(q, k_pages, k_pages, np.array([[1]]), np.array([0]), 0.1)
+    assert (o == 0).all() and np.isneginf(lse).all()
