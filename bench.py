@@ -164,7 +164,12 @@ def main():
     import exact_attention_115_amd as fa
     from synth import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    # A trailing "p" on a decode workload (c5dgp, c5dmp) runs it over a paged
+    # K/V cache: 128-key pages in a shuffled pool, every sequence full.
+    paged = args.workload.endswith("p") and args.workload[:-1] in WORKLOADS
+    w = WORKLOADS[args.workload[:-1] if paged else args.workload]
+    if paged and w.Nq != 1:
+        raise SystemExit("paged workloads are decode workloads")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     if args.copy_mib > 0:
@@ -182,6 +187,26 @@ def main():
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
     fws = fa.fa_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, q.dtype)
     fwd_ws = torch.empty(fws, dtype=torch.uint8, device=dev) if fws else None
+    if paged:
+        PS = 128
+        mp = (w.Nkv + PS - 1) // PS
+        npages = w.B * mp
+        pad = mp * PS - w.Nkv
+        kpad = torch.nn.functional.pad(k, (0, 0, 0, pad))
+        vpad = torch.nn.functional.pad(v, (0, 0, 0, pad))
+        perm = torch.randperm(npages, generator=torch.Generator().manual_seed(w.seed)).to(dev)
+        k_pool = torch.empty((npages, w.Hkv, PS, w.d), dtype=k.dtype, device=dev)
+        v_pool = torch.empty_like(k_pool)
+        # Logical page p of sequence b goes to pool page perm[b * mp + p].
+        k_pool[perm] = kpad.reshape(w.B, w.Hkv, mp, PS, w.d).permute(0, 2, 1, 3, 4).reshape(
+            npages, w.Hkv, PS, w.d)
+        v_pool[perm] = vpad.reshape(w.B, w.Hkv, mp, PS, w.d).permute(0, 2, 1, 3, 4).reshape(
+            npages, w.Hkv, PS, w.d)
+        table = perm.reshape(w.B, mp).to(torch.int32).contiguous()
+        lens = torch.full((w.B,), w.Nkv, dtype=torch.int32, device=dev)
+        del kpad, vpad
+        pws = fa.fa_fwd_paged_workspace_size(w.B, w.Hq, w.Hkv, PS, mp, w.d, q.dtype)
+        fwd_ws = torch.empty(pws, dtype=torch.uint8, device=dev)
     bwd = w.backward
     if bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -193,7 +218,10 @@ def main():
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        st = fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream)
+        if paged:
+            st = fa.fa_fwd_paged(q, k_pool, v_pool, table, lens, o, lse, fwd_ws, w.scale, stream)
+        else:
+            st = fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream)
         if st != 0:
             raise fa.FAError(st, "fa_fwd")
         if events is not None:
@@ -240,7 +268,7 @@ def main():
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
     out = {
-        "metric": METRIC if args.workload == "c3" else f"attention throughput, {w.name}",
+        "metric": METRIC if args.workload == "c3" else f"attention throughput, {args.workload}",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -252,7 +280,9 @@ def main():
         "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to the storage dtype",
         "config": {"workload": f"{'causal' if w.causal else 'non-causal'} attention "
                                f"{'forward+backward' if bwd else 'forward'} B={w.B} Hq={w.Hq} "
-                               f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}",
+                               f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}"
+                               + (" over a paged K/V cache (128-key pages, shuffled pool)"
+                                  if paged else ""),
                    "name": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N_q": w.Nq,
                    "N_kv": w.Nkv, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
@@ -260,13 +290,13 @@ def main():
     }
     if w.Nq == 1:
         # Decode: HBM-bound, reported as algorithmic bytes per second.
-        nbytes = decode_bytes(w)
+        nbytes = decode_bytes(w) + ((table.numel() + lens.numel()) * 4 if paged else 0)
         gbs = nbytes / (ms_per_step * 1e-3) / 1e9
         out.update({"value": round(gbs, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                     "cache": "cold (1 GiB write before each timed call)" if cold else "warm"})
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                           "kernel": "decode split + combine (one fa_fwd call)",
+                           "kernel": "decode split + combine (one fa_fwd" + ("_paged" if paged else "") + " call)",
                            "algorithmic_bytes": nbytes}
     else:
         tflops = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
