@@ -34,6 +34,9 @@ Modules
 
 ``reference.paged_decode_forward`` is decode over a paged K/V cache: the keys
 of each sequence gathered through its page-table row, then the definition.
+``dropout``    dropout on the probabilities with a mask drawn from the
+               counter-based generator Philox4x64-10 (readings in its
+               docstring), forward and backward.
 
 Readings of the pages where they are silent are listed in ``reference``.
 Parity status: every function here is pinned by a CPU test in
@@ -50,6 +53,14 @@ from .reference import (  # noqa: F401
     paged_decode_forward,
     paged_gather,
     visible_mask,
+)
+from .dropout import (  # noqa: F401
+    attention_backward_dropout,
+    attention_forward_dropout,
+    keep_mask,
+    keep_scale,
+    philox4x64,
+    threshold,
 )
 from .online import online_row, online_forward  # noqa: F401
 from .brute import brute_forward  # noqa: F401

@@ -341,3 +341,139 @@ def test_paged_decode_empty_sequence():
     q = rng.standard_normal((1, 2, 1, 64))
     o, lse = oracle.paged_decode_forward(q, k_pages, k_pages, np.array([[1]]), np.array([0]), 0.1)
     assert (o == 0).all() and np.isneginf(lse).all()
+
+
+# ------------------------------------------------------------------- dropout
+
+from oracle import dropout as drop  # noqa: E402
+
+
+def test_philox_matches_numpy_generator():
+    """The oracle's Philox4x64-10 against numpy.random.Philox, an independent
+    implementation of the same published generator. numpy advances its
+    counter by one before producing the first 256-bit block."""
+    rng = np.random.default_rng(11)
+    counters = rng.integers(0, 2**63, size=(300, 4), dtype=np.uint64)
+    keys = rng.integers(0, 2**64 - 1, size=(300, 2), dtype=np.uint64, endpoint=True)
+    counters[:5] = 0
+    keys[:5] = [[0, 0], [2**64 - 1, 2**64 - 1], [1, 0], [0, 1], [123456789, 987654321]]
+    counters[5:10, 1:] = 2**64 - 1  # large words in every position but the incremented one
+    for c, k in zip(counters, keys):
+        expect = np.random.Philox(counter=c, key=k).random_raw(4)
+        c1 = c.copy()
+        c1[0] += np.uint64(1)
+        got = drop.philox4x64(c1, k)
+        assert np.array_equal(got, expect), (c, k)
+    # Vectorised call over many counters equals the one-by-one results.
+    c1 = counters.copy()
+    c1[:, 0] += np.uint64(1)
+    batch = drop.philox4x64(c1, keys)
+    for i in range(0, 300, 37):
+        assert np.array_equal(batch[i], np.random.Philox(counter=counters[i], key=keys[i]).random_raw(4))
+
+
+def test_dropout_bytes_come_from_the_documented_counter():
+    """Byte t of key group g of row i of head bh is byte t % 8 of word t // 8
+    of philox((g, i, bh, offset), (seed, 0)) (checked on a few elements with
+    direct generator calls)."""
+    seed, offset, bh = 987, 4, 7
+    u = drop.dropout_bytes(bh, np.arange(5), 100, seed, offset)
+    for i, j in [(0, 0), (1, 31), (2, 32), (4, 99), (3, 70)]:
+        w = drop.philox4x64(np.array([j // 32, i, bh, offset], dtype=np.uint64),
+                            np.array([seed, 0], dtype=np.uint64))
+        t = j % 32
+        assert u[i, j] == (int(w[t // 8]) >> (8 * (t % 8))) & 0xFF
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
+def test_dropout_keep_rate(p):
+    """Kept fraction within 5 standard deviations of 1 - theta / 256."""
+    z = drop.keep_mask(3, np.arange(256), 512, p, seed=2024, offset=1)
+    q = 1.0 - drop.threshold(p) / 256.0
+    sd = math.sqrt(q * (1 - q) / z.size)
+    assert abs(z.mean() - q) <= 5 * sd
+    # No structure along rows or columns: per-column rates stay within 6 sd.
+    col = z.mean(axis=0)
+    assert np.max(np.abs(col - q)) <= 6 * math.sqrt(q * (1 - q) / z.shape[0])
+
+
+def test_dropout_masks_differ_across_heads_seeds_offsets():
+    base = drop.keep_mask(0, np.arange(64), 256, 0.5, 1, 0)
+    for other in (drop.keep_mask(1, np.arange(64), 256, 0.5, 1, 0),
+                  drop.keep_mask(0, np.arange(64), 256, 0.5, 2, 0),
+                  drop.keep_mask(0, np.arange(64), 256, 0.5, 1, 1)):
+        agree = np.mean(base == other)
+        assert 0.45 < agree < 0.55  # independent masks agree about half the time
+
+
+def test_dropout_threshold_and_scale():
+    assert drop.threshold(0.0) == 0 and drop.keep_scale(0.0) == 1.0
+    assert drop.threshold(0.25) == 64 and drop.keep_scale(0.25) == pytest.approx(256 / 192)
+    assert drop.threshold(0.999) == 255
+    with pytest.raises(ValueError):
+        drop.threshold(1.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_zero_probability_is_the_plain_definition(causal):
+    q, k, v, do = rnd((2, 4, 7, 5), 60), rnd((2, 2, 9, 5), 61), rnd((2, 2, 9, 5), 62), rnd((2, 4, 7, 5), 63)
+    o, lse = drop.attention_forward_dropout(q, k, v, causal, 0.6, 0.0, 5, 0)
+    o_ref, lse_ref = oracle.attention_forward(q, k, v, causal, 0.6)
+    np.testing.assert_allclose(o, o_ref, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-14)
+    for g, g_ref in zip(drop.attention_backward_dropout(q, k, v, do, causal, 0.6, 0.0, 5, 0),
+                        oracle.attention_backward(q, k, v, do, causal, 0.6)):
+        np.testing.assert_allclose(g, g_ref, atol=1e-13)
+
+
+def test_dropout_keeps_lse_and_scales_kept_terms():
+    """LSE ignores the mask; with V = identity, row i of O is r P_i o Z_i."""
+    q, k = rnd((6, 8), 64), rnd((8, 8), 65)
+    z = drop.keep_mask(0, np.arange(6), 8, 0.3, 9, 0)
+    r = drop.keep_scale(0.3)
+    o, lse = drop.head_forward_dropout(q, k, np.eye(8), False, 0.5, z, r)
+    o0, lse0 = oracle.head_forward(q, k, np.eye(8), False, 0.5)
+    np.testing.assert_allclose(lse, lse0, atol=1e-14)
+    np.testing.assert_allclose(o, r * o0 * z, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_gradients_by_finite_differences(causal):
+    """With the mask fixed, O is a smooth function of q, k, v: central
+    differences of sum(dO * O) match the analytic gradients."""
+    rng = np.random.default_rng(66)
+    nq, nkv, d = 5, 7, 3
+    q, k, v, do = (rng.standard_normal(s) for s in [(nq, d), (nkv, d), (nkv, d), (nq, d)])
+    z = rng.random((nq, nkv)) < 0.6
+    r, scale = 1.7, 0.8
+    grads = drop.head_backward_dropout(q, k, v, do, causal, scale, z, r)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * drop.head_forward_dropout(qq, kk, vv, causal, scale, z, r)[0]))
+
+    h = 1e-6
+    for which, g in enumerate(grads):
+        base = [q, k, v]
+        fd = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert np.linalg.norm(g - fd) / np.linalg.norm(fd) <= 1e-6, which
+
+
+def test_dropout_row_term_identity():
+    """rowsum(P o dP) = rowsum(dO o O) still holds with dropout (what lets the
+    backward use D = rowsum(dO o O))."""
+    rng = np.random.default_rng(67)
+    q, k, v, do = (rng.standard_normal(s) for s in [(6, 4), (9, 4), (9, 4), (6, 4)])
+    z = rng.random((6, 9)) < 0.5
+    r = 2.0
+    o, _ = drop.head_forward_dropout(q, k, v, False, 0.9, z, r)
+    s = 0.9 * (q @ k.T)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = r * z * (do @ v.T)
+    np.testing.assert_allclose(np.sum(p * dp, axis=1), np.sum(do * o, axis=1), atol=1e-12)
