@@ -68,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_paged_workspace_size.restype = sz
     lib.fa_fwd_paged.argtypes = [vp] * 8 + [sz] + [i] * 7 + [f, i, vp]
     lib.fa_fwd_paged.restype = i
+    u64 = ctypes.c_uint64
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, sz] + shape + [f, i, f, u64, u64, i, vp]
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_dropout_mask.argtypes = [vp, i, i, i, i, f, u64, u64, vp]
+    lib.fa_dropout_mask.restype = i
     _lib = lib
     return lib
 
@@ -246,3 +251,54 @@ def forward_paged(q, k_pages, v_pages, page_table, seq_lens, scale: float | None
     if st != FA_OK:
         raise FAError(st, "fa_fwd_paged")
     return o, lse
+
+
+# ------------------------------------------------------------------ dropout
+
+def fa_fwd_dropout(q, k, v, o, lse, workspace, scale: float, causal: bool, dropout_p: float,
+                   seed: int, offset: int = 0, stream=None) -> int:
+    """Call fa_fwd_dropout on tensors; returns the status code (no exception)."""
+    _check({"q": q, "k": k, "v": v, "o": o}, q.dtype)
+    _check({"lse": lse}, torch.float32)
+    _check({"workspace": workspace})
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                 ws_bytes, B, Hq, Hkv, Nq, Nkv, d, float(scale),
+                                 int(bool(causal)), float(dropout_p), int(seed), int(offset),
+                                 _dtype_code(q), _stream(stream))
+
+
+def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, causal: bool = False,
+                    scale: float | None = None, stream=None):
+    """O, LSE of attention with dropout on P (see fa_fwd_dropout in fa.h).
+    Allocates o, lse and the workspace."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    ws = _workspace(fa_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, q.dtype), q.device)
+    st = fa_fwd_dropout(q, k, v, o, lse, ws, _default_scale(d, scale), causal, dropout_p, seed,
+                        offset, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def fa_dropout_mask(keep, B: int, Hq: int, Nq: int, Nkv: int, dropout_p: float, seed: int,
+                    offset: int = 0, stream=None) -> int:
+    """Call fa_dropout_mask into a uint8 tensor [B, Hq, Nq, Nkv]; returns the status."""
+    _check({"keep": keep}, torch.uint8)
+    if keep is not None and keep.numel() < B * Hq * Nq * Nkv:
+        raise ValueError("keep is smaller than B * Hq * Nq * Nkv bytes")
+    return load().fa_dropout_mask(_ptr(keep), int(B), int(Hq), int(Nq), int(Nkv),
+                                  float(dropout_p), int(seed), int(offset), _stream(stream))
+
+
+def dropout_mask(B: int, Hq: int, Nq: int, Nkv: int, dropout_p: float, seed: int, offset: int = 0,
+                 device="cuda", stream=None):
+    """The keep mask of fa_fwd_dropout as a uint8 tensor [B, Hq, Nq, Nkv] (1 = kept)."""
+    keep = torch.empty((B, Hq, Nq, Nkv), dtype=torch.uint8, device=device)
+    st = fa_dropout_mask(keep, B, Hq, Nq, Nkv, dropout_p, seed, offset, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_dropout_mask")
+    return keep

@@ -28,6 +28,7 @@ SOURCES = [
     "fa_decode.hip",
     "fa_bwd.hip",
     "fa_bwd_dq.hip",
+    "fa_dropout.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -172,6 +172,19 @@ BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, 
   return t;
 }
 
+// Dropout parameters from the probability: theta = min(255, floor(256 p + 1/2)),
+// rscale = 256 / (256 - theta). p must be finite and in [0, 1).
+int drop_params(float p, uint64_t seed, uint64_t offset, DropParams* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return FA_ERR_SCALE;  // also rejects NaN
+  double t = floor(256.0 * (double)p + 0.5);
+  if (t > 255.0) t = 255.0;
+  out->seed = seed;
+  out->offset = offset;
+  out->theta = (uint32_t)t;
+  out->rscale = (float)(256.0 / (256.0 - t));
+  return FA_OK;
+}
+
 int run_bwd_stage(int stage, const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   switch (stage) {
     case 0: return to_status(launch_bwd_pre(p, t, stream));
@@ -346,6 +359,37 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     if (st != FA_OK) return st;
   }
   return FA_OK;
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nkv,
+                   int d, float scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,
+                   fa_dtype dt, hipStream_t stream) {
+  bool empty = false;
+  Problem p;
+  int st = check_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nkv, d, scale,
+                     causal, dt, &empty, &p);
+  if (st != FA_OK) return st;
+  if (dt == FA_F32) return FA_ERR_UNSUPPORTED;
+  DropParams dp;
+  st = drop_params(dropout_p, seed, offset, &dp);
+  if (st != FA_OK || empty) return st;
+  FwdPtrs t{q, k, v, o, lse, workspace};
+  // Every query length, one row included, takes the tiled kernel.
+  return to_status(launch_fwd_mfma(p, t, stream, &dp));
+}
+
+int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float dropout_p,
+                    uint64_t seed, uint64_t offset, hipStream_t stream) {
+  if (B < 0 || Hq < 0 || Nq < 0 || Nkv < 0) return FA_ERR_SHAPE;
+  DropParams dp;
+  int st = drop_params(dropout_p, seed, offset, &dp);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq * Nq * Nkv == 0) return FA_OK;
+  if ((long long)B * Hq >= (1LL << 31) || (double)B * Hq * Nq * Nkv >= 4.0e18)
+    return FA_ERR_UNSUPPORTED;
+  if (!keep) return FA_ERR_NULLPTR;
+  return to_status(launch_dropout_mask(keep, B, Hq, Nq, Nkv, dp, stream));
 }
 
 size_t fa_fwd_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages, int d,

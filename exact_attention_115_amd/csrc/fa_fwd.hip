@@ -65,7 +65,14 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
   float scale_log2;
+  DropParams drop;  // used only by the dropout instantiations
 };
+
+// x if bit b of the keep word kw is set, else +0 (dropout).
+__device__ __forceinline__ float keep_f(float x, uint32_t kw, int b) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
+                                       (uint32_t)((int32_t)(kw << (31 - b)) >> 31));
+}
 
 // S^T = K Q^T for the 64 keys of the K tile at ks (DMA layout; kb0, kb1:
 // this lane's k_read_base for even and odd kc): two 32-key blocks,
@@ -89,15 +96,21 @@ __device__ __forceinline__ void qk_tile(const uint8_t* ks, uint32_t kb0, uint32_
 
 // P = exp2(S * scale_log2 - m) rounded to 16 bits, pk[4 ch + t] holding the
 // keys 16 ch + 8 h + 2t, +1 of this lane's row (the B operand of chunk ch of
-// O^T += V^T P^T); returns this lane's sum of the unrounded values.
-template <typename T>
-__device__ __forceinline__ float exp_tile(const f32x16* s, float sl2, float m, uint32_t* pk) {
+// O^T += V^T P^T); returns this lane's sum of the unrounded values. With
+// dropout, values whose bit of kw (bit 2i, 2i + 1 for pair i) is clear enter
+// P as zero but still count in the sum.
+template <typename T, bool DROP = false>
+__device__ __forceinline__ float exp_tile(const f32x16* s, float sl2, float m, uint32_t* pk,
+                                          uint32_t kw = ~0u) {
   float psum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7)], sl2, -m));
     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i >> 3][2 * (i & 7) + 1], sl2, -m));
-    pk[i] = pack2<T>(p0, p1);
+    if constexpr (DROP)
+      pk[i] = pack2<T>(keep_f(p0, kw, 2 * i), keep_f(p1, kw, 2 * i + 1));
+    else
+      pk[i] = pack2<T>(p0, p1);
     psum += p0 + p1;
   }
   return psum;
@@ -112,12 +125,14 @@ __device__ __forceinline__ float exp_tile(const f32x16* s, float sl2, float m, u
 // Matrix-core products alternate between the two products; every product's
 // LDS operands are read two products ahead; each product is followed by its
 // share of the exponentials; scheduling fences keep that order. Returns this
-// lane's sum of the (unrounded) exponentials.
-template <typename T, int D>
+// lane's sum of the (unrounded) exponentials. With dropout, kw is the keep
+// word of tile i + 1 (see exp_tile).
+template <typename T, int D, bool DROP = false>
 __device__ __forceinline__ float fused_tile(const uint8_t* kt, uint32_t kr0, uint32_t kr1,
                                    const typename T::vec8* qf, f32x16* sn, const uint8_t* vt,
                                    uint32_t vr, const uint32_t* pc, f32x16* oacc,
-                                   const f32x16* se, float sl2, float m, uint32_t* pn) {
+                                   const f32x16* se, float sl2, float m, uint32_t* pn,
+                                   uint32_t kw = ~0u) {
   using V8 = typename T::vec8;
   constexpr int RB = DmaTile<D>::RB;
   constexpr int OD = D / 32;
@@ -162,14 +177,20 @@ __device__ __forceinline__ float fused_tile(const uint8_t* kt, uint32_t kr0, uin
         e0 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7)], sl2, -m));
         e1 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7) + 1], sl2, -m));
       } else {
-        pn[e] = pack2<T>(e0, e1);
+        if constexpr (DROP)
+          pn[e] = pack2<T>(keep_f(e0, kw, 2 * e), keep_f(e1, kw, 2 * e + 1));
+        else
+          pn[e] = pack2<T>(e0, e1);
         psum += e0 + e1;
       }
     } else {  // one pair per product
       const int e = t;
       const float p0 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7)], sl2, -m));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(se[e >> 3][2 * (e & 7) + 1], sl2, -m));
-      pn[e] = pack2<T>(p0, p1);
+      if constexpr (DROP)
+        pn[e] = pack2<T>(keep_f(p0, kw, 2 * e), keep_f(p1, kw, 2 * e + 1));
+      else
+        pn[e] = pack2<T>(p0, p1);
       psum += p0 + p1;
     }
     // Keep the running sum in step (otherwise its adds drift to the end).
@@ -194,7 +215,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Key/value tiles go through two LDS buffers each, loaded directly from
 // global memory. Step i of the software pipeline reads K tile i + 2 and V
 // tile i while the loads of K tile i + 3 and V tile i + 1 are in flight.
-template <typename T, int D, bool CAUSAL, int NW>
+//
+// DROP: dropout on P (keep words from keep_bits, one generator call per lane
+// per tile; the two half-waves exchange the halves of their key groups), O
+// scaled by 1 / (1 - p) at the end.
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   constexpr int BR = 32 * NW;       // query rows per workgroup
   using V8 = typename T::vec8;
@@ -293,7 +318,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   // When the exponentials p of scores s (taken against m_run) summed to more
   // than kSumLimit in some row: move the maximum to the true running maximum,
   // rescale what U and l hold, and redo p. Returns the new sum.
-  auto fix_max = [&](const f32x16* s, uint32_t* p, float psum) __attribute__((always_inline)) {
+  auto fix_max = [&](const f32x16* s, uint32_t* p, float psum, uint32_t kw)
+                     __attribute__((always_inline)) {
     if (__builtin_expect(__any(!(psum <= kSumLimit)), 0)) {
       float mx = -INFINITY;
 #pragma unroll
@@ -309,9 +335,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[od][r] *= alpha;
       m_run = m_new;
-      psum = exp_tile<T>(s, sl2, (m_new == -INFINITY) ? 0.0f : m_new, p);
+      psum = exp_tile<T, DROP>(s, sl2, (m_new == -INFINITY) ? 0.0f : m_new, p, kw);
     }
     return psum;
+  };
+
+  // Dropout keep word of tile j for this lane: bit 16 kb + r is key
+  // 64 j + 32 kb + acc_key(h, r). Half h draws key group 2 j + h (keys
+  // 64 j + 32 h ..) and the halves swap what the other needs.
+  auto keep_word = [&](int j) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!DROP) {
+      return ~0u;
+    } else {
+      const uint32_t own = keep_bits((uint32_t)(2 * j + h), (uint32_t)qrow, (uint32_t)bh, a.drop);
+      const uint32_t other = (uint32_t)__shfl_xor((int)own, 32, 64);
+      const uint32_t g0 = h ? other : own, g1 = h ? own : other;
+      const int sh = 8 * h;
+      return ((g0 >> sh) & 0xFFu) | (((g0 >> (16 + sh)) & 0xFFu) << 8) |
+             (((g1 >> sh) & 0xFFu) << 16) | (((g1 >> (16 + sh)) & 0xFFu) << 24);
+    }
   };
 
   // Pipeline state entering step i: scores of tile i + 1 and the 16-bit P of
@@ -330,7 +372,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   if (n_w > 0) {
     qk_tile<T, D>(kbuf0, kr0, kr1, qf, sa);
     mask_tile(0, sa);
-    l_run += fix_max(sa, pa, exp_tile<T>(sa, sl2, m_run, pa));
+    const uint32_t kw0 = keep_word(0);
+    l_run += fix_max(sa, pa, exp_tile<T, DROP>(sa, sl2, m_run, pa, kw0), kw0);
     qk_tile<T, D>(kbuf1, kr0, kr1, qf, sb);
   }
   __syncthreads();
@@ -344,9 +387,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   auto step = [&](int i, f32x16* se, const uint32_t* pc, f32x16* sn, uint32_t* pn,
                   const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     const bool live = i + 1 < n_w;  // is there a tile i + 1 for this wave?
-    if (live) mask_tile(i + 1, se);
-    float psum = fused_tile<T, D>(kt, kr0, kr1, qf, sn, vt, vr, pc, oacc, se, sl2, m_run, pn);
-    if (live) l_run += fix_max(se, pn, psum);
+    uint32_t kw = ~0u;
+    if (live) {
+      mask_tile(i + 1, se);
+      kw = keep_word(i + 1);
+    }
+    float psum = fused_tile<T, D, DROP>(kt, kr0, kr1, qf, sn, vt, vr, pc, oacc, se, sl2, m_run, pn, kw);
+    if (live) l_run += fix_max(se, pn, psum, kw);
   };
 
   // Every wave runs n_tiles (loads, barrier) rounds and computes the first
@@ -375,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   // Epilogue: O = U / l, LSE = m + ln l (natural log).
   const float l = l_run + swap_halves(l_run);
   if (qrow < Nq) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = l > 0.0f ? (DROP ? a.drop.rscale : 1.0f) / l : 0.0f;
     uint16_t* orow = a.o + (bh * Nq + qrow) * D;
 #pragma unroll
     for (int od = 0; od < OD; ++od)
@@ -390,8 +437,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int NW>
-hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+template <typename T, int D, int NW, bool DROP>
+hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream, const DropParams* dp) {
   constexpr int BR = 32 * NW;
   FwdArgs a;
   a.q = static_cast<const uint16_t*>(t.q);
@@ -407,11 +454,12 @@ hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
   a.Nkv = p.Nkv;
   a.n_qtiles = (p.Nq + BR - 1) / BR;
   a.scale_log2 = p.scale * LOG2E;
+  a.drop = dp ? *dp : DropParams{0, 0, 0, 1.0f};
   dim3 grid(a.n_qtiles * p.B * p.Hq);
   if (p.causal)
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, true, NW, DROP>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, false, NW, DROP>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -419,20 +467,27 @@ hipError_t launch_nw(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
 // long (N_q >= 4096), else 128-row ones: on shorter sequences two workgroups
 // per CU overlap one's start-up with the other's main loop, which outweighs
 // sharing each K/V tile among 8 waves instead of 4.
-template <typename T, int D>
-hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+template <typename T, int D, bool DROP>
+hipError_t launch_drop(const Problem& p, const FwdPtrs& t, hipStream_t stream, const DropParams* dp) {
   const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
-  return (big_tiles >= 256 && p.Nq >= 4096) ? launch_nw<T, D, 8>(p, t, stream)
-                                            : launch_nw<T, D, 4>(p, t, stream);
+  return (big_tiles >= 256 && p.Nq >= 4096) ? launch_nw<T, D, 8, DROP>(p, t, stream, dp)
+                                            : launch_nw<T, D, 4, DROP>(p, t, stream, dp);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Problem& p, const FwdPtrs& t, hipStream_t stream, const DropParams* dp) {
+  return dp ? launch_drop<T, D, true>(p, t, stream, dp) : launch_drop<T, D, false>(p, t, stream, dp);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
+hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream,
+                           const DropParams* dp) {
   if (p.dt == FA_BF16) {
-    return p.d == 64 ? launch_typed<BF16, 64>(p, t, stream) : launch_typed<BF16, 128>(p, t, stream);
+    return p.d == 64 ? launch_typed<BF16, 64>(p, t, stream, dp)
+                     : launch_typed<BF16, 128>(p, t, stream, dp);
   }
-  return p.d == 64 ? launch_typed<F16, 64>(p, t, stream) : launch_typed<F16, 128>(p, t, stream);
+  return p.d == 64 ? launch_typed<F16, 64>(p, t, stream, dp) : launch_typed<F16, 128>(p, t, stream, dp);
 }
 
 }  // namespace fa

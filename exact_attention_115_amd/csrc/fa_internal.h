@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_philox.h"
 
 namespace fa {
 
@@ -69,9 +70,13 @@ int bwd_group_split(const Problem& p);
 // Launchers: each enqueues its kernel(s) on `stream` and returns the
 // hipError_t of the launch.
 hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream);
-hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+// drop: dropout parameters, or null for none.
+hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream,
+                           const DropParams* drop = nullptr);
 hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream);
 hipError_t launch_decode_paged(const Problem& p, const FwdPtrs& t, const PagedPtrs& pg,
+                               hipStream_t stream);
+hipError_t launch_dropout_mask(uint8_t* keep, int B, int Hq, int Nq, int Nkv, const DropParams& dp,
                                hipStream_t stream);
 hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);

@@ -1,0 +1,80 @@
+// Dropout keep bits from the counter-based generator Philox4x64-10
+// (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+// 3", SC 2011). Dropout acts on the attention probabilities, a step page
+// [KB] "FlashAttention：为什么少搬数据，反而算得更快" §04 lists among those the tiled
+// computation must still handle; as with P itself ([KB] §05) the mask is
+// rebuilt where it is needed and never stored.
+//
+// Element (b, h, i, j) -- query head h, query row i, key j -- takes byte
+// t = j mod 32 of the 256-bit block philox(counter, key) with
+// counter = (j / 32, i, b * Hq + h, offset) and key = (seed, 0); byte t is
+// bits 8 (t mod 8) .. +7 of output word t / 8. The element is kept iff that
+// byte is >= theta. keep_bits() returns the 32 decisions of one key group as
+// a word (bit t: key 32 * group + t).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct DropParams {
+  uint64_t seed;
+  uint64_t offset;
+  uint32_t theta;  // keep iff byte >= theta (0 keeps everything)
+  float rscale;    // 256 / (256 - theta)
+};
+
+// The four output words of Philox4x64-10 for counter c and key (k0, k1).
+__host__ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t hi0 = __umul64hi(M0, c[0]), hi1 = __umul64hi(M1, c[2]);
+#else
+    const uint64_t hi0 = (uint64_t)(((unsigned __int128)M0 * c[0]) >> 64);
+    const uint64_t hi1 = (uint64_t)(((unsigned __int128)M1 * c[2]) >> 64);
+#endif
+    const uint64_t lo0 = M0 * c[0], lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// Bit b of the result (b = 0..3) is 1 iff byte b of x is >= the byte y8
+// (y4 = y8 replicated in all four bytes). Per byte: with the top bits set
+// aside, (x | 0x80) - (y & 0x7f) keeps its top bit iff the low seven bits of
+// x are >= those of y, and no borrow crosses bytes; the top bits of x and y
+// then decide (x wins if only x has it, ties fall to the low bits).
+__host__ __device__ __forceinline__ uint32_t bytes_ge4(uint32_t x, uint32_t y4) {
+  constexpr uint32_t H = 0x80808080u;
+  const uint32_t z = (x | H) - (y4 & ~H);
+  const uint32_t ge = ((x & ~y4) | (~(x ^ y4) & z)) & H;
+  // Gather the four top bits (positions 7, 15, 23, 31) into bits 0..3.
+  return ((ge >> 7) * 0x00204081u) >> 21 & 0xFu;
+}
+
+// The keep decisions of keys 32 * group .. 32 * group + 31 of query row `row`
+// of head bh (= b * Hq + h).
+__host__ __device__ __forceinline__ uint32_t keep_bits(uint32_t group, uint32_t row, uint32_t bh,
+                                                       const DropParams& dp) {
+  uint64_t c[4] = {group, row, bh, dp.offset};
+  philox4x64_10(c, dp.seed, 0);
+  const uint32_t y4 = dp.theta * 0x01010101u;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t x = (uint32_t)(c[w >> 1] >> (32 * (w & 1)));
+    bits |= bytes_ge4(x, y4) << (4 * w);
+  }
+  return bits;
+}
+
+}  // namespace fa

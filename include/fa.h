@@ -50,6 +50,7 @@
 #define FA_H_
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -154,6 +155,40 @@ int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
  * problem). */
 size_t fa_fwd_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
                                    fa_dtype dt);
+
+/* Dropout on the attention probabilities ([KB] §04 lists dropout among what
+ * the tiled computation must still get right; [KB] §08's example call carries
+ * a dropout probability). Inverted dropout on the normalised P, with keep
+ * mask Z:
+ *   O = r (P o Z) V,  r = 256 / (256 - theta),  theta = min(255, floor(256 p + 1/2)),
+ * and lse exactly as fa_fwd (the mask does not enter it). Like P ([KB] §05)
+ * the mask is never stored: element (b, h, i, j) -- query head h, query row
+ * i, key j -- is kept iff byte t = j mod 32 of the 256-bit block of the
+ * counter-based generator Philox4x64-10 (Salmon, Moraes, Dror, Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) for counter
+ * (floor(j / 32), i, b * Hq + h, offset) and key (seed, 0) is >= theta, byte
+ * t being bits 8 (t mod 8) .. +7 of output word floor(t / 8). A caller draws
+ * a fresh mask by changing seed or offset; the backward of one forward must
+ * use the same (dropout_p, seed, offset).
+ * dropout_p: finite, 0 <= p < 1 (else FA_ERR_SCALE); p = 0 gives fa_fwd's
+ * result. FA_F16 and FA_BF16 only (FA_F32: FA_ERR_UNSUPPORTED). All other
+ * arguments, the workspace (size from fa_fwd_workspace_size) and the status
+ * codes are those of fa_fwd; asynchronous on stream. */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                   float scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,
+                   fa_dtype dt, hipStream_t stream);
+
+/* The keep mask Z of fa_fwd_dropout for the same (dropout_p, seed, offset),
+ * written out as bytes: keep [B, Hq, N_q, N_kv] uint8 in device memory, 1 =
+ * kept, 0 = dropped, every byte written (also where the causal mask hides the
+ * key). For tests and debugging: the attention calls draw the same bits and
+ * never write them. No alignment requirement. FA_ERR_SCALE for a bad
+ * dropout_p, FA_ERR_SHAPE for a negative size, FA_ERR_UNSUPPORTED when
+ * B * Hq >= 2^31; empty sizes return FA_OK. Asynchronous on stream. */
+int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float dropout_p,
+                    uint64_t seed, uint64_t offset, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -186,3 +186,35 @@ def test_paged_rejects_bad_arguments():
     assert paged(o=P(1)) == -8                # output aliases q
     assert paged(ws=P(4)) == -8               # workspace aliases the page table
     assert paged(B=0) == 0                    # nothing to do
+
+
+def fwd_drop(p=0.1, seed=1, offset=0, **kw):
+    a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), ws=None, ws_bytes=0, B=1, Hq=2, Hkv=2,
+             Nq=64, Nkv=64, d=64, scale=0.125, causal=0, dt=fa.FA_BF16)
+    a.update(kw)
+    return fa.load().fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"],
+                                    a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"],
+                                    a["d"], a["scale"], a["causal"], p, seed, offset, a["dt"], None)
+
+
+def test_fwd_dropout_rejects_bad_arguments():
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert fwd_drop(p=p) == -6, p
+    assert fwd_drop(dt=fa.FA_F32) == -3
+    assert fwd_drop(q=None) == -1
+    assert fwd_drop(d=96) == -3
+    assert fwd_drop(Hq=3, Hkv=2) == -2
+    assert fwd_drop(scale=0.0) == -6
+    assert fwd_drop(o=P(1)) == -8
+    assert fwd_drop(Nq=0) == 0            # empty problem: nothing enqueued
+    assert fwd_drop(Nq=0, p=2.0) == -6    # but the probability is still checked
+
+
+def test_dropout_mask_rejects_bad_arguments():
+    lib = fa.load()
+    assert lib.fa_dropout_mask(P(1), 1, 2, 3, 4, 1.0, 1, 0, None) == -6
+    assert lib.fa_dropout_mask(P(1), 1, 2, 3, 4, float("nan"), 1, 0, None) == -6
+    assert lib.fa_dropout_mask(P(1), -1, 2, 3, 4, 0.5, 1, 0, None) == -2
+    assert lib.fa_dropout_mask(None, 1, 2, 3, 4, 0.5, 1, 0, None) == -1
+    assert lib.fa_dropout_mask(None, 1, 2, 0, 4, 0.5, 1, 0, None) == 0
+    assert lib.fa_dropout_mask(P(1), 1 << 16, 1 << 16, 1, 1, 0.5, 1, 0, None) == -3
