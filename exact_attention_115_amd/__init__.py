@@ -4,9 +4,10 @@ split-KV decode in hand-written HIP kernels behind a C ABI (include/fa.h).
 Python names mirror the C entry points (``fa_fwd``, ``fa_bwd``,
 ``fa_bwd_stage``, ``fa_fwd_workspace_size``, ``fa_bwd_workspace_size``,
 ``fa_fwd_paged``, ``fa_fwd_paged_workspace_size``, ``fa_fwd_dropout``,
-``fa_dropout_mask``, ``fa_strerror``, ``fa_version``); ``forward``,
-``backward``, ``forward_paged``, ``forward_dropout`` and ``dropout_mask``
-allocate the outputs and the workspace and raise on error.
+``fa_bwd_dropout``, ``fa_dropout_mask``, ``fa_strerror``, ``fa_version``);
+``forward``, ``backward``, ``forward_paged``, ``forward_dropout``,
+``backward_dropout`` and ``dropout_mask`` allocate the outputs and the
+workspace and raise on error.
 """
 
 from ._lib import (  # noqa: F401
@@ -17,7 +18,9 @@ from ._lib import (  # noqa: F401
     FAError,
     LIB_PATH,
     backward,
+    backward_dropout,
     fa_bwd,
+    fa_bwd_dropout,
     fa_bwd_stage,
     fa_bwd_workspace_size,
     fa_dropout_mask,

@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
     u64 = ctypes.c_uint64
     lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, sz] + shape + [f, i, f, u64, u64, i, vp]
     lib.fa_fwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = bwd[:-2] + [f, u64, u64, i, vp]
+    lib.fa_bwd_dropout.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, i, f, u64, u64, vp]
     lib.fa_dropout_mask.restype = i
     _lib = lib
@@ -282,6 +284,26 @@ def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, causa
     if st != FA_OK:
         raise FAError(st, "fa_fwd_dropout")
     return o, lse
+
+
+def fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, workspace, scale: float, causal: bool,
+                   dropout_p: float, seed: int, offset: int = 0, stream=None) -> int:
+    """Call fa_bwd_dropout on tensors; returns the status code (no exception)."""
+    args = _bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream)
+    return load().fa_bwd_dropout(*args[:-2], float(dropout_p), int(seed), int(offset), *args[-2:])
+
+
+def backward_dropout(q, k, v, o, lse, do, dropout_p: float, seed: int, offset: int = 0,
+                     causal: bool = False, scale: float | None = None, stream=None):
+    """dq, dk, dv for forward_dropout with the same (dropout_p, seed, offset)."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = _workspace(fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, q.dtype), q.device)
+    st = fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, ws, _default_scale(d, scale), causal,
+                        dropout_p, seed, offset, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dropout")
+    return dq, dk, dv
 
 
 def fa_dropout_mask(keep, B: int, Hq: int, Nq: int, Nkv: int, dropout_p: float, seed: int,

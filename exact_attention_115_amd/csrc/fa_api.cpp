@@ -163,6 +163,7 @@ BwdPtrs bwd_ptrs(const Problem& p, const void* q, const void* k, const void* v, 
   t.nd = reinterpret_cast<float*>(base);
   t.lneg = base ? reinterpret_cast<float*>(base + del) : nullptr;
   t.dk_part = t.dv_part = nullptr;
+  t.drop = nullptr;
   const int gs = bwd_group_split(p);
   if (gs > 1 && base) {
     const size_t part = align_up((size_t)gs * p.B * p.Hkv * p.Nkv * p.d * sizeof(float), 256);
@@ -377,6 +378,28 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   FwdPtrs t{q, k, v, o, lse, workspace};
   // Every query length, one row included, takes the tiled kernel.
   return to_status(launch_fwd_mfma(p, t, stream, &dp));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                   float scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,
+                   fa_dtype dt, hipStream_t stream) {
+  bool empty = false;
+  Problem p;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq,
+                     Nkv, d, scale, causal, dt, &empty, &p);
+  if (st != FA_OK) return st;
+  DropParams dp;
+  st = drop_params(dropout_p, seed, offset, &dp);
+  if (st != FA_OK || empty) return st;
+  BwdPtrs t = bwd_ptrs(p, q, k, v, o, lse, dO, dq, dk, dv, workspace);
+  t.drop = &dp;
+  for (int stage = 0; stage < 3; ++stage) {
+    st = run_bwd_stage(stage, p, t, stream);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
 }
 
 int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float dropout_p,

@@ -62,11 +62,12 @@ struct BwdArgs {
   float* dv_part;
   int Hq, Hkv, G, Nq, Nkv, n_kblocks, n_bk, gsplit;
   float scale, scale_log2;
+  DropParams drop;  // used only by the dropout instantiations
 };
 
 // ---------------------------------------------------------------- stage 0
-// nd_i = -D_i = -sum_c dO_ic O_ic in float32, and lneg_i = -LSE_i / scale
-// (-inf for a row that saw no key). Starting the S accumulator of row i at
+// nd_i = -D_i = -sum_c dO_ic O_ic in float32 (-D_i / r with dropout, r the
+// keep factor), and lneg_i = -LSE_i / scale (-inf for a row that saw no key). Starting the S accumulator of row i at
 // lneg_i and the dP accumulator at nd_i leaves S - LSE / scale and dP - D in
 // them, so P = exp2(scale log2(e) acc) and dS = P acc' need no further
 // per-row terms.
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ nd,
                                                       float* __restrict__ lneg, size_t rows,
-                                                      float inv_scale) {
+                                                      float inv_scale, float inv_r) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int RPB = NTB / CPR;
   const int t = threadIdx.x;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && ch == 0) {
-    nd[row] = -acc;
+    nd[row] = -acc * inv_r;
     const float l = lse[row];
     lneg[row] = l == -INFINITY ? -INFINITY : -l * inv_scale;
   }
@@ -159,13 +160,18 @@ __device__ __forceinline__ void xdl_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\
 // the order. Element pair e of a lane is keys' query rows 32 (e / 8) +
 // acc_key(h, 2 (e % 8)), +1 (consecutive), and pc[4 ch + t] / dsc[4 ch + t]
 // hold query rows 16 ch + 8 h + 2t, +1: the B operands of chunk ch.
-template <typename T, int D, bool PREV>
+//
+// DROP (dropout, keep word kw: bit 2e, 2e + 1 for pair e): P enters dV as
+// P o Z, and dS / r = P (Z ? dP' : -D / r) with the dP accumulators started
+// from -D / r (dnc: tile i's -D / r rows); the factor r is applied to dK and
+// dV at the end.
+template <typename T, int D, bool PREV, bool DROP = false>
 __device__ __forceinline__ void dkdv_step(
     const uint8_t* qn, const uint8_t* gn, const uint8_t* qp, const uint8_t* gp, uint32_t kr0,
     uint32_t kr1, uint32_t kt0, uint32_t kt1, typename T::vec8* kf, typename T::vec8* vf,
     f32x16* sn, f32x16* dpn, f32x16* dk, f32x16* dv, const uint32_t* pp, const uint32_t* dsp,
     const f32x16* s, const f32x16* dpc, const float* ln, const float* dn, int h, float sl2,
-    uint32_t* pc, uint32_t* dsc) {
+    uint32_t* pc, uint32_t* dsc, uint32_t kw = ~0u, const float* dnc = nullptr) {
   using V8 = typename T::vec8;
   constexpr int RB = DmaTile<D>::RB;
   constexpr int KC = D / 16;
@@ -231,10 +237,19 @@ __device__ __forceinline__ void dkdv_step(
         e0 = __builtin_amdgcn_exp2f(s[kb][r] * sl2);
         e1 = __builtin_amdgcn_exp2f(s[kb][r + 1] * sl2);
       } else if (part == 1) {
-        pc[e] = pack2<T>(e0, e1);
+        if constexpr (DROP)
+          pc[e] = pack2<T>(keep_f(e0, kw, 2 * e), keep_f(e1, kw, 2 * e + 1));
+        else
+          pc[e] = pack2<T>(e0, e1);
       } else if (part == 2) {
-        e0 = e0 * dpc[kb][r];
-        e1 = e1 * dpc[kb][r + 1];
+        if constexpr (DROP) {
+          const f32x2 nv = *reinterpret_cast<const f32x2*>(dnc + kb * 32 + acc_key(h, r));
+          e0 = e0 * (((kw >> (2 * e)) & 1u) ? dpc[kb][r] : nv[0]);
+          e1 = e1 * (((kw >> (2 * e + 1)) & 1u) ? dpc[kb][r + 1] : nv[1]);
+        } else {
+          e0 = e0 * dpc[kb][r];
+          e1 = e1 * dpc[kb][r + 1];
+        }
       } else {
         dsc[e] = pack2<T>(e0, e1);
       }
@@ -301,7 +316,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // i + 1 (row terms) and tile i - 1 (transposed). One wave per SIMD: the stationary
 // K, V, the dK, dV accumulators and two tiles of scores and P need more than
 // the 256 registers two waves per SIMD would leave.
-template <typename T, int D, bool CAUSAL>
+//
+// DROP: dropout. Each tile's keep bits are drawn once per lane (lane l: query
+// row l of the tile, the wave's 32 keys) and turned through LDS into the
+// lane = key layout.
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using V8 = typename T::vec8;
   using DT = DmaTile<D, 4>;
@@ -320,6 +339,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t gs3[TB];
   __shared__ __attribute__((aligned(256))) float ls0[BQ], ls1[BQ], ls2[BQ], ls3[BQ];
   __shared__ __attribute__((aligned(256))) float ds0[BQ], ds1[BQ], ds2[BQ], ds3[BQ];
+  __shared__ __attribute__((aligned(256))) uint32_t kwbuf[DROP ? 4 * BQ : 4];
   auto qslot = [&](int x) __attribute__((always_inline)) -> uint8_t* {
     return x == 0 ? qs0 : x == 1 ? qs1 : x == 2 ? qs2 : qs3;
   };
@@ -425,6 +445,37 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // Dropout keep word of tile t for this lane (bit 16 qb + r: query row
+  // qb * 32 + acc_key(h, r) of the tile, key my_key). Lane l draws row l's
+  // decisions for the wave's 32 keys; the words go through this wave's LDS
+  // block, and each lane picks its key's bit from its 32 rows.
+  auto keep_word = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (!DROP) {
+      return ~0u;
+    } else {
+      const int hq = hq0 + t / per_head;
+      const int qi0 = (qt_begin + t % per_head) * BQ;
+      const uint32_t w = keep_bits((uint32_t)(kw0 >> 5), (uint32_t)(qi0 + lane),
+                                   (uint32_t)(b * a.Hq + hq), a.drop);
+      uint32_t* buf = kwbuf + wave * BQ;
+      buf[lane] = w;
+      __builtin_amdgcn_wave_barrier();
+      uint32_t kw = 0;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int run = 0; run < 2; ++run)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(buf + qb * 32 + run * 16 + 8 * h + 4 * half);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kw |= ((x[j] >> c) & 1u) << (16 * qb + 8 * run + 4 * half + j);
+          }
+      __builtin_amdgcn_wave_barrier();
+      return kw;
+    }
+  };
+
   // Pipeline state entering step i: scores and dP of tile i, P and dS of tile
   // i - 1. Tile t's scores live in sa/da and its P, dS in pa/za when t is
   // even, in sb/db and pb/zb when t is odd.
@@ -440,10 +491,11 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     tile_rows<T, D>(qs0, kr0, kr1, kf, ls0, h, sa);
     tile_rows<T, D>(gs0, kr0, kr1, vf, ds0, h, da);
     load_tile(2, 2);
+    const uint32_t kwt = keep_word(0);
     xdl_wait();
     mask_tile(0, sa);
-    dkdv_step<T, D, false>(qs1, gs1, qs3, gs3, kr0, kr1, kt0, kt1, kf, vf, sb, db, dk, dv, pb, zb,
-                           sa, da, ls1, ds1, h, sl2, pa, za);
+    dkdv_step<T, D, false, DROP>(qs1, gs1, qs3, gs3, kr0, kr1, kt0, kt1, kf, vf, sb, db, dk, dv, pb,
+                                 zb, sa, da, ls1, ds1, h, sl2, pa, za, kwt, ds0);
   }
   __syncthreads();
 
@@ -461,12 +513,14 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
         load_tile(i + 2, (r + 3) & 3);
         f32x16* s = even ? sa : sb;
         f32x16* dpc = even ? da : db;
+        const uint32_t kwt = keep_word(i);
         xdl_wait();  // the scores and dP of tile i were written last step
         mask_tile(i, s);
-        dkdv_step<T, D, true>(qslot((r + 2) & 3), gslot((r + 2) & 3), qslot(r & 3), gslot(r & 3),
-                              kr0, kr1, kt0, kt1, kf, vf, even ? sb : sa, even ? db : da, dk, dv,
-                              even ? pb : pa, even ? zb : za, s, dpc, lslot((r + 2) & 3),
-                              dslot((r + 2) & 3), h, sl2, even ? pa : pb, even ? za : zb);
+        dkdv_step<T, D, true, DROP>(qslot((r + 2) & 3), gslot((r + 2) & 3), qslot(r & 3),
+                                    gslot(r & 3), kr0, kr1, kt0, kt1, kf, vf, even ? sb : sa,
+                                    even ? db : da, dk, dv, even ? pb : pa, even ? zb : za, s, dpc,
+                                    lslot((r + 2) & 3), dslot((r + 2) & 3), h, sl2, even ? pa : pb,
+                                    even ? za : zb, kwt, dslot((r + 1) & 3));
         __syncthreads();
       }
     });
@@ -480,7 +534,17 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   xdl_wait();
 
   // ---- dK = scale * (sum dS^T Q) and dV (lane = key, 16 dims per tile); a
-  // split head group writes float32 partial sums that stage 2 adds up.
+  // split head group writes float32 partial sums that stage 2 adds up. With
+  // dropout both carry the keep factor r.
+  if constexpr (DROP) {
+#pragma unroll
+    for (int od = 0; od < OD; ++od)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dk[od][i] *= a.drop.rscale;
+        dv[od][i] *= a.drop.rscale;
+      }
+  }
   if (my_key < Nkv) {
     const size_t row = (size_t)bk * Nkv + my_key;
     if (a.gsplit == 1) {
@@ -576,6 +640,7 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.n_bk = p.B * p.Hkv;
   a.scale = p.scale;
   a.scale_log2 = p.scale * LOG2E;
+  a.drop = t.drop ? *t.drop : DropParams{0, 0, 0, 1.0f};
   return a;
 }
 
@@ -587,7 +652,7 @@ hipError_t pre_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, dim3(NTB), 0, stream,
                      static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.lse,
-                     t.nd, t.lneg, rows, 1.0f / p.scale);
+                     t.nd, t.lneg, rows, 1.0f / p.scale, t.drop ? 1.0f / t.drop->rscale : 1.0f);
   return hipGetLastError();
 }
 
@@ -596,10 +661,17 @@ hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const BwdArgs a = make_args(p, t);
   if (a.n_kblocks == 0 || a.n_bk == 0) return hipSuccess;
   dim3 grid((unsigned)(a.n_kblocks * a.n_bk * a.gsplit));
-  if (p.causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, dim3(NTB), 0, stream, a);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, dim3(NTB), 0, stream, a);
+  if (t.drop) {
+    if (p.causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), grid, dim3(NTB), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), grid, dim3(NTB), 0, stream, a);
+  } else {
+    if (p.causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), grid, dim3(NTB), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), grid, dim3(NTB), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

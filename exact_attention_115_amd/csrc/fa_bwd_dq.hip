@@ -39,11 +39,16 @@ struct DqArgs {
   uint16_t* dq;
   int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
   float scale, scale_log2;
+  DropParams drop;  // used only by the dropout instantiations
 };
 
 // NW waves of 32 query rows per workgroup (8 when the grid fills the GPU,
 // else 4), as in the forward.
-template <typename T, int D, bool CAUSAL, int NW>
+//
+// DROP: dropout with keep factor r; the first stage stored -D / r in nd, so
+// dS / r = P ((Z ? dP : 0) - D / r), and dQ carries r at the end. The keep
+// words are drawn as in the forward.
+template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   constexpr int BR = 32 * NW;
   using V8 = typename T::vec8;
@@ -132,6 +137,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   // LDS operands are read two products ahead.
   auto compute = [&](int j, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     constexpr int RB = DT::RB;
+    uint32_t kw = ~0u;
+    if constexpr (DROP) kw = row_keep_word(j, (uint32_t)qrow, (uint32_t)bh, h, a.drop);
     f32x16 s[2], dp[2];
     auto rfrag = [&](const uint8_t* xs, int q) {
       const int kb = q / KC, kc = q % KC;
@@ -169,7 +176,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
     };
     auto ds_pair = [&](int e) __attribute__((always_inline)) {
       const int kb = e >> 3, r = 2 * (e & 7);
-      ds[e] = pack2<T>(s[kb][r] * (dp[kb][r] + ndrow), s[kb][r + 1] * (dp[kb][r + 1] + ndrow));
+      if constexpr (DROP)
+        ds[e] = pack2<T>(s[kb][r] * (keep_f(dp[kb][r], kw, 2 * e) + ndrow),
+                         s[kb][r + 1] * (keep_f(dp[kb][r + 1], kw, 2 * e + 1) + ndrow));
+      else
+        ds[e] = pack2<T>(s[kb][r] * (dp[kb][r] + ndrow), s[kb][r + 1] * (dp[kb][r + 1] + ndrow));
     };
     dp[0] = zero16();
     dp[1] = zero16();
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   // rows = dims).
   if (has_row) {
     uint16_t* row = a.dq + (bh * Nq + qrow) * D;
-    const float sc = a.scale;
+    const float sc = DROP ? a.scale * a.drop.rscale : a.scale;
 #pragma unroll
     for (int od = 0; od < OD; ++od)
 #pragma unroll
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool DROP>
 hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   DqArgs a;
   a.q = static_cast<const uint16_t*>(t.q);
@@ -266,19 +277,21 @@ hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   a.n_qtiles = (p.Nq + 32 * NW - 1) / (32 * NW);
   a.scale = p.scale;
   a.scale_log2 = p.scale * LOG2E;
+  a.drop = t.drop ? *t.drop : DropParams{0, 0, 0, 1.0f};
   dim3 grid((unsigned)(a.n_qtiles * p.B * p.Hq));
   if (p.causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, NW, DROP>), grid, dim3(64 * NW), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, NW, DROP>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const long long big_tiles = (long long)p.B * p.Hq * ((p.Nq + 255) / 256);
-  return (big_tiles >= 256 && p.Nq >= 4096) ? launch_nw<T, D, 8>(p, t, stream)
-                                            : launch_nw<T, D, 4>(p, t, stream);
+  const bool big = big_tiles >= 256 && p.Nq >= 4096;
+  if (t.drop) return big ? launch_nw<T, D, 8, true>(p, t, stream) : launch_nw<T, D, 4, true>(p, t, stream);
+  return big ? launch_nw<T, D, 8, false>(p, t, stream) : launch_nw<T, D, 4, false>(p, t, stream);
 }
 
 }  // namespace

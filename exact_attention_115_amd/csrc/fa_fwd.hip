@@ -68,11 +68,6 @@ struct FwdArgs {
   DropParams drop;  // used only by the dropout instantiations
 };
 
-// x if bit b of the keep word kw is set, else +0 (dropout).
-__device__ __forceinline__ float keep_f(float x, uint32_t kw, int b) {
-  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
-                                       (uint32_t)((int32_t)(kw << (31 - b)) >> 31));
-}
 
 // S^T = K Q^T for the 64 keys of the K tile at ks (DMA layout; kb0, kb1:
 // this lane's k_read_base for even and odd kc): two 32-key blocks,
@@ -340,20 +335,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
     return psum;
   };
 
-  // Dropout keep word of tile j for this lane: bit 16 kb + r is key
-  // 64 j + 32 kb + acc_key(h, r). Half h draws key group 2 j + h (keys
-  // 64 j + 32 h ..) and the halves swap what the other needs.
+  // Dropout keep word of tile j for this lane (bit 16 kb + r: key
+  // 64 j + 32 kb + acc_key(h, r)).
   auto keep_word = [&](int j) __attribute__((always_inline)) -> uint32_t {
-    if constexpr (!DROP) {
+    if constexpr (!DROP)
       return ~0u;
-    } else {
-      const uint32_t own = keep_bits((uint32_t)(2 * j + h), (uint32_t)qrow, (uint32_t)bh, a.drop);
-      const uint32_t other = (uint32_t)__shfl_xor((int)own, 32, 64);
-      const uint32_t g0 = h ? other : own, g1 = h ? own : other;
-      const int sh = 8 * h;
-      return ((g0 >> sh) & 0xFFu) | (((g0 >> (16 + sh)) & 0xFFu) << 8) |
-             (((g1 >> sh) & 0xFFu) << 16) | (((g1 >> (16 + sh)) & 0xFFu) << 24);
-    }
+    else
+      return row_keep_word(j, (uint32_t)qrow, (uint32_t)bh, h, a.drop);
   };
 
   // Pipeline state entering step i: scores of tile i + 1 and the 16-bit P of

@@ -51,6 +51,7 @@ struct BwdPtrs {
   float* lneg;       // [B, Hq, Nq] float32 -LSE / scale (-inf: no key), in the workspace
   float* dk_part;    // [gsplit, B, Hkv, Nkv, d] float32 partial sums, or NULL
   float* dv_part;    //   (present only when the head group is split)
+  const DropParams* drop;  // dropout parameters, or NULL for none
 };
 
 // Decode (N_q == 1) split-KV geometry, shared by the workspace size and the

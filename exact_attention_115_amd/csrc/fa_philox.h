@@ -77,4 +77,26 @@ __host__ __device__ __forceinline__ uint32_t keep_bits(uint32_t group, uint32_t 
   return bits;
 }
 
+// x if bit b of the keep word kw is set, else +0.
+__device__ __forceinline__ float keep_f(float x, uint32_t kw, int b) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
+                                       (uint32_t)((int32_t)(kw << (31 - b)) >> 31));
+}
+
+// Keep word of the 64-key tile j for a lane of the transposed-score layout
+// (lane (h, c) holds query row `row`; its accumulator r of key block kb is
+// key 64 j + 32 kb + 8 h + r for r < 8 and 64 j + 32 kb + 16 + 8 h + r - 8
+// otherwise): bit 16 kb + r is that key's decision. Half h draws key group
+// 2 j + h and the two halves swap the bytes the other needs; all 64 lanes
+// must take part.
+__device__ __forceinline__ uint32_t row_keep_word(int j, uint32_t row, uint32_t bh, int h,
+                                                  const DropParams& dp) {
+  const uint32_t own = keep_bits((uint32_t)(2 * j + h), row, bh, dp);
+  const uint32_t other = (uint32_t)__shfl_xor((int)own, 32, 64);
+  const uint32_t g0 = h ? other : own, g1 = h ? own : other;
+  const int sh = 8 * h;
+  return ((g0 >> sh) & 0xFFu) | (((g0 >> (16 + sh)) & 0xFFu) << 8) |
+         (((g1 >> sh) & 0xFFu) << 16) | (((g1 >> (16 + sh)) & 0xFFu) << 24);
+}
+
 }  // namespace fa

@@ -168,13 +168,29 @@ size_t fa_fwd_paged_workspace_size(int B, int Hq, int Hkv, int page_size, int ma
  * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) for counter
  * (floor(j / 32), i, b * Hq + h, offset) and key (seed, 0) is >= theta, byte
  * t being bits 8 (t mod 8) .. +7 of output word floor(t / 8). A caller draws
- * a fresh mask by changing seed or offset; the backward of one forward must
- * use the same (dropout_p, seed, offset).
+ * a fresh mask by changing seed or offset; the backward (fa_bwd_dropout) of
+ * one forward must use the same (dropout_p, seed, offset).
  * dropout_p: finite, 0 <= p < 1 (else FA_ERR_SCALE); p = 0 gives fa_fwd's
  * result. FA_F16 and FA_BF16 only (FA_F32: FA_ERR_UNSUPPORTED). All other
  * arguments, the workspace (size from fa_fwd_workspace_size) and the status
  * codes are those of fa_fwd; asynchronous on stream. */
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                   float scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,
+                   fa_dtype dt, hipStream_t stream);
+
+/* Backward of fa_fwd_dropout, for the same (dropout_p, seed, offset): the
+ * keep mask is drawn again, tile by tile, exactly as the forward drew it, and
+ * with r and Z as above
+ *   dV = r (P o Z)^T dO,  dP = r Z o (dO V^T),  dS = P * (dP - D),
+ *   D_i = sum_c dO_ic O_ic (still equal to sum_j P_ij dP_ij),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * o and lse are fa_fwd_dropout's outputs. dropout_p: finite, 0 <= p < 1
+ * (else FA_ERR_SCALE). Otherwise the arguments, workspace (size from
+ * fa_bwd_workspace_size) and status codes are those of fa_bwd. */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                    float scale, int causal, float dropout_p, uint64_t seed, uint64_t offset,

@@ -218,3 +218,25 @@ def test_dropout_mask_rejects_bad_arguments():
     assert lib.fa_dropout_mask(None, 1, 2, 3, 4, 0.5, 1, 0, None) == -1
     assert lib.fa_dropout_mask(None, 1, 2, 0, 4, 0.5, 1, 0, None) == 0
     assert lib.fa_dropout_mask(P(1), 1 << 16, 1 << 16, 1, 1, 0.5, 1, 0, None) == -3
+
+
+def test_bwd_dropout_rejects_bad_arguments():
+    lib = fa.load()
+
+    def call(p=0.1, **kw):
+        a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), do=P(6), dq=P(7), dk=P(8), dv=P(9),
+                 ws=P(10), ws_bytes=1 << 30, B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=64, scale=0.125,
+                 causal=0, dt=fa.FA_BF16)
+        a.update(kw)
+        return lib.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                  a["dk"], a["dv"], a["ws"], a["ws_bytes"], a["B"], a["Hq"],
+                                  a["Hkv"], a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], p,
+                                  7, 0, a["dt"], None)
+
+    for p in (-0.5, 1.0, float("nan")):
+        assert call(p=p) == -6, p
+    assert call(dt=fa.FA_F32) == -3
+    assert call(do=None) == -1
+    assert call(ws=None) == -1
+    assert call(dq=P(1)) == -8
+    assert call(B=0) == 0

@@ -1,11 +1,12 @@
-"""GPU parity of dropout (fa_fwd_dropout, fa_dropout_mask) against the
-float64 oracle in oracle/dropout.py.
+"""GPU parity of dropout (fa_fwd_dropout, fa_bwd_dropout, fa_dropout_mask)
+against the float64 oracle in oracle/dropout.py.
 
 The keep mask is integer work and must match bit for bit. Outputs use the
 forward's 16-bit bar scaled by r = 1 / (1 - p_eff): every kept probability,
 and so O itself, is multiplied by r before the output is rounded, so the
 rounding error (a fixed number of units in the last place of O) grows by the
-same factor. LSE does not depend on the mask and keeps its own bar.
+same factor. LSE does not depend on the mask and keeps its own bar. Gradients
+keep the relative bar of the plain backward (it is scale-free).
 """
 
 import numpy as np
@@ -123,3 +124,74 @@ def test_forward_dropout_repeatable_and_mask_dependent():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert not torch.equal(a[0], c[0])
     assert torch.equal(a[1], c[1])  # LSE does not depend on the mask
+
+
+# ------------------------------------------------------------------ backward
+
+def check_dropout_grads(grads, q, k, v, do, causal, scale, p, seed, offset, dtype, label):
+    g_ref = drop.attention_backward_dropout(to_f64(q), to_f64(k), to_f64(v), to_f64(do), causal,
+                                            scale, f32(p), seed, offset)
+    tol = TOL[dtype]["grad_rel"]
+    for name, g, r in zip(("dq", "dk", "dv"), grads, g_ref):
+        gg = to_f64(g)
+        assert np.all(np.isfinite(gg)), name
+        rel = float(np.linalg.norm(gg - r) / max(np.linalg.norm(r), 1e-30))
+        say(f"  [{label}] {name} Frobenius rel {rel:.3e}")
+        assert rel <= tol, (name, rel)
+
+
+BWD_CASES = [
+    # B, Hq, Hkv, Nq, Nkv, d, causal, dtype, p
+    (1, 4, 2, 200, 300, 64, True, "bf16", 0.2),
+    (2, 4, 4, 130, 130, 128, False, "f16", 0.5),
+    (1, 8, 1, 160, 96, 128, True, "bf16", 0.3),     # MQA: split head group, float32 partials
+    (1, 8, 2, 1000, 1000, 128, True, "bf16", 0.1),
+    (3, 6, 3, 65, 129, 64, True, "f16", 0.75),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(c) for c in BWD_CASES])
+def test_backward_dropout_parity(case):
+    B, Hq, Hkv, Nq, Nkv, d, causal, dtype, p = case
+    scale = 1.0 / np.sqrt(d)
+    seed, offset = 4321 + Nkv, 9
+    say(f"backward dropout {case}")
+    q, k, v, do = random_tensors((B, Hq, Nq, d), (B, Hkv, Nkv, d), dtype, seed=81, with_grad=True)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = fa.forward_dropout(qg, kg, vg, p, seed, offset, causal=causal, scale=scale)
+    grads = fa.backward_dropout(qg, kg, vg, o, lse, dog, p, seed, offset, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    check_dropout_grads(grads, q, k, v, do, causal, scale, p, seed, offset, dtype, str(case))
+
+
+def test_backward_dropout_zero_probability_equals_backward():
+    q, k, v, do = random_tensors((2, 4, 300, 128), (2, 2, 300, 128), "bf16", seed=82, with_grad=True)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = fa.forward(qg, kg, vg, causal=True)
+    a = fa.backward(qg, kg, vg, o, lse, dog, causal=True)
+    b = fa.backward_dropout(qg, kg, vg, o, lse, dog, 0.0, 5, 0, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_dropout_long_sampled():
+    """Long causal case (the 256-row dQ workgroups, 8 waves) on a reduced head
+    count; the oracle's gradients are computed per head for two heads."""
+    w = WORKLOADS["c3"].replace(name="drop_bwd_long", Hq=16, Hkv=16, Nq=4096, Nkv=4096, seed=40)
+    p, seed, offset = 0.2, 17, 2
+    q, k, v, do = make_inputs(w, with_grad=True)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = fa.forward_dropout(qg, kg, vg, p, seed, offset, causal=True, scale=w.scale)
+    dq, dk, dv = fa.backward_dropout(qg, kg, vg, o, lse, dog, p, seed, offset, causal=True,
+                                     scale=w.scale)
+    torch.cuda.synchronize()
+    r = drop.keep_scale(f32(p))
+    for h in (0, w.Hq - 1):
+        z = drop.keep_mask(h, np.arange(w.Nq), w.Nkv, f32(p), seed, offset)
+        g_ref = drop.head_backward_dropout(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]),
+                                           to_f64(do[0, h]), True, w.scale, z, r)
+        for name, g, ref in zip(("dq", "dk", "dv"), (dq[0, h], dk[0, h], dv[0, h]), g_ref):
+            rel = float(np.linalg.norm(to_f64(g) - ref) / np.linalg.norm(ref))
+            say(f"  [long head {h}] {name} Frobenius rel {rel:.3e}")
+            assert rel <= TOL[w.dtype]["grad_rel"], (h, name, rel)
