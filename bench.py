@@ -70,6 +70,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the warmup")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P (fa_fwd_dropout / fa_bwd_dropout); the "
+                         "backward is then timed as one pass")
     ap.add_argument("--warm-cache", action="store_true",
                     help="decode workloads: skip the cache flush before each timed call")
     return ap.parse_args()
@@ -213,11 +216,33 @@ def main():
         bws = fa.fa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, q.dtype)
         bwd_ws = torch.empty(bws, dtype=torch.uint8, device=dev)
 
-    names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if bwd else [])
+    drop = args.dropout > 0.0
+    if drop and (paged or w.Nq == 1):
+        raise SystemExit("--dropout applies to the prefill workloads")
+    if drop:
+        names = ["fwd"] + (["bwd"] if bwd else [])
+    else:
+        names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if bwd else [])
+    seed = 1234
 
     def step(events=None):
         if events is not None:
             events[0].record(stream)
+        if drop:
+            st = fa.fa_fwd_dropout(q, k, v, o, lse, fwd_ws, w.scale, w.causal, args.dropout, seed,
+                                   0, stream)
+            if st != 0:
+                raise fa.FAError(st, "fa_fwd_dropout")
+            if events is not None:
+                events[1].record(stream)
+            if bwd:
+                st = fa.fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale, w.causal,
+                                       args.dropout, seed, 0, stream)
+                if st != 0:
+                    raise fa.FAError(st, "fa_bwd_dropout")
+                if events is not None:
+                    events[2].record(stream)
+            return
         if paged:
             st = fa.fa_fwd_paged(q, k_pool, v_pool, table, lens, o, lse, fwd_ws, w.scale, stream)
         else:
@@ -268,7 +293,9 @@ def main():
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
     out = {
-        "metric": METRIC if args.workload == "c3" else f"attention throughput, {args.workload}",
+        "metric": (METRIC if args.workload == "c3" and not drop
+                   else f"attention throughput, {args.workload}"
+                   + (f" with dropout p={args.dropout}" if drop else "")),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -282,7 +309,8 @@ def main():
                                f"{'forward+backward' if bwd else 'forward'} B={w.B} Hq={w.Hq} "
                                f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}"
                                + (" over a paged K/V cache (128-key pages, shuffled pool)"
-                                  if paged else ""),
+                                  if paged else "")
+                               + (f" with dropout p={args.dropout} on P" if drop else ""),
                    "name": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N_q": w.Nq,
                    "N_kv": w.Nkv, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
@@ -306,12 +334,16 @@ def main():
                     "fwd_tflops": round(fwd_t, 2),
                     "fwd_pct_peak": round(100 * fwd_t / PEAK_BF16_TFLOPS, 2)})
         flop = {"fwd": fwd_flop}
-        if bwd:
+        if bwd and drop:
+            bwd_t = bwd_flop / (per_kernel_ms["bwd"] * 1e-3) / 1e12
+            out.update({"bwd_tflops": round(bwd_t, 2), "bwd_pct_peak": round(100 * bwd_t / PEAK_BF16_TFLOPS, 2)})
+            flop["bwd"] = bwd_flop
+        elif bwd:
             bwd_ms = per_kernel_ms["bwd_pre"] + per_kernel_ms["bwd_dkdv"] + per_kernel_ms["bwd_dq"]
             bwd_t = bwd_flop / (bwd_ms * 1e-3) / 1e12
             out.update({"bwd_tflops": round(bwd_t, 2), "bwd_pct_peak": round(100 * bwd_t / PEAK_BF16_TFLOPS, 2)})
             flop.update({"bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop})
-        on_profiled = args.workload == "c3"
+        on_profiled = args.workload == "c3" and not drop
         lines = {kname: mfma_roofline(kname, f, per_kernel_ms[kname],
                                       read_traffic(kname) if on_profiled else None)
                  for kname, f in flop.items()}
@@ -319,7 +351,7 @@ def main():
         dom = max(lines, key=lambda kname: per_kernel_ms[kname])
         out["roofline"] = lines[dom]
         out["roofline_all"] = lines
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not drop:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
