@@ -34,6 +34,9 @@ Modules
 
 ``reference.paged_decode_forward`` is decode over a paged K/V cache: the keys
 of each sequence gathered through its page-table row, then the definition.
+``fp8``        the forward of E4M3 (8-bit float) inputs with per-tensor
+               descale factors: their decoded values, then the definition;
+               and the bound on what rounding P to E4M3 may change in O.
 ``dropout``    dropout on the probabilities with a mask drawn from the
                counter-based generator Philox4x64-10 (readings in its
                docstring), forward and backward.
@@ -62,5 +65,6 @@ from .dropout import (  # noqa: F401
     philox4x64,
     threshold,
 )
+from .fp8 import decode as fp8_decode, head_forward_fp8, p_rounding_bound  # noqa: F401
 from .online import online_row, online_forward  # noqa: F401
 from .brute import brute_forward  # noqa: F401

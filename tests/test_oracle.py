@@ -477,3 +477,56 @@ def test_dropout_row_term_identity():
     p /= p.sum(axis=1, keepdims=True)
     dp = r * z * (do @ v.T)
     np.testing.assert_allclose(np.sum(p * dp, axis=1), np.sum(do * o, axis=1), atol=1e-12)
+
+
+# ---------------------------------------------------------------------- fp8
+
+from oracle import fp8 as f8  # noqa: E402
+import torch  # noqa: E402
+
+
+def test_e4m3_table_matches_torch_float8():
+    """The oracle's E4M3 decode (written from the format definition) against
+    torch's float8_e4m3fn conversion, an independent implementation."""
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(t)
+    assert np.array_equal(nan, np.isnan(f8.E4M3_TABLE))
+    assert np.array_equal(t[~nan], f8.E4M3_TABLE[~nan])
+    assert f8.e4m3_value(0x38) == 1.0 and f8.e4m3_value(0x7E) == 448.0
+    assert f8.e4m3_value(0x01) == 2.0 ** -9 and f8.e4m3_value(0x08) == 2.0 ** -6
+    assert np.isnan(f8.e4m3_value(0x7F)) and np.isnan(f8.e4m3_value(0xFF))
+
+
+def test_fp8_forward_is_the_definition_on_decoded_inputs():
+    rng = np.random.default_rng(90)
+    q8, k8, v8 = (rng.integers(0, 256, size=s, dtype=np.uint8) for s in [(9, 16), (12, 16), (12, 16)])
+    for a in (q8, k8, v8):
+        a[(a & 0x7F) == 0x7F] = 0x30  # no NaN codes
+    o, lse = f8.head_forward_fp8(q8, k8, v8, True, 0.25, 0.5, 0.125, 2.0)
+    o_ref, lse_ref = oracle.head_forward(f8.decode(q8) * 0.5, f8.decode(k8) * 0.125,
+                                         f8.decode(v8) * 2.0, True, 0.25)
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(lse, lse_ref)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_p_rounding_bound_holds_for_rounded_p(causal):
+    """Rounding P (relative to the row maximum) to E4M3 with an independent
+    rounder (torch) moves O by no more than p_rounding_bound."""
+    rng = np.random.default_rng(91)
+    nq, nkv, d = 40, 300, 32
+    vals = torch.from_numpy(rng.standard_normal((nq + 2 * nkv, d))).to(torch.float8_e4m3fn)
+    codes = vals.view(torch.uint8).numpy()
+    q8, k8, v8 = codes[:nq], codes[nq:nq + nkv], codes[nq + nkv:]
+    scale, dq, dk, dv = 0.3, 1.0, 1.0, 1.0
+    q, k, v = f8.decode(q8), f8.decode(k8), f8.decode(v8)
+    s = scale * (q @ k.T)
+    vis = oracle.visible_mask(np.arange(nq), nq, nkv, causal)
+    s = np.where(vis, s, -np.inf)
+    e = np.exp(s - s.max(axis=1, keepdims=True))          # values relative to the row max
+    e8 = torch.from_numpy(e).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    o_rounded = (e8 @ v) / e.sum(axis=1, keepdims=True)
+    o_exact, _ = f8.head_forward_fp8(q8, k8, v8, causal, scale, dq, dk, dv)
+    bound = f8.p_rounding_bound(q8, k8, v8, causal, scale, dq, dk, dv)
+    assert np.all(np.abs(o_rounded - o_exact) <= bound + 1e-12)
+    assert np.max(np.abs(o_rounded - o_exact)) > 0  # the rounding is visible
