@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak (published)
 METRIC = "attention fwd/bwd TFLOP/s & % bf16 MFMA peak, causal N=4096 d=128"
 CSRC = os.path.join(ROOT, "exact_attention_115_amd", "csrc")
 COMMON = ["fa_device.h", "fa_tile.h", "fa_internal.h"]
@@ -73,6 +74,9 @@ def parse():
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability on P (fa_fwd_dropout / fa_bwd_dropout); the "
                          "backward is then timed as one pass")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 (E4M3) forward (fa_fwd_fp8) on the workload's shape, "
+                         "forward only")
     ap.add_argument("--warm-cache", action="store_true",
                     help="decode workloads: skip the cache flush before each timed call")
     return ap.parse_args()
@@ -146,10 +150,10 @@ def decode_bytes(w):
             + 4 * w.B * w.Hq * w.Nq)
 
 
-def mfma_roofline(kernel, flop, ms, traffic):
+def mfma_roofline(kernel, flop, ms, traffic, peak=PEAK_BF16_TFLOPS):
     ach = flop / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
             "kernel": kernel, "avg_launch_ms": round(ms, 4),
             "algorithmic_flop_per_launch": flop}
 
@@ -219,6 +223,16 @@ def main():
     drop = args.dropout > 0.0
     if drop and (paged or w.Nq == 1):
         raise SystemExit("--dropout applies to the prefill workloads")
+    fp8 = args.fp8
+    if fp8:
+        if paged or w.Nq == 1 or w.d != 128 or drop:
+            raise SystemExit("--fp8 applies to the d = 128 prefill workloads, without dropout")
+        # E4M3 codes of the same draws (descale 1), bf16 output.
+        q8 = q.float().to(torch.float8_e4m3fn).view(torch.uint8)
+        k8 = k.float().to(torch.float8_e4m3fn).view(torch.uint8)
+        v8 = v.float().to(torch.float8_e4m3fn).view(torch.uint8)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        bwd = False
     if drop:
         names = ["fwd"] + (["bwd"] if bwd else [])
     else:
@@ -228,6 +242,13 @@ def main():
     def step(events=None):
         if events is not None:
             events[0].record(stream)
+        if fp8:
+            st = fa.fa_fwd_fp8(q8, k8, v8, o, lse, w.scale, w.causal, 1.0, 1.0, 1.0, stream)
+            if st != 0:
+                raise fa.FAError(st, "fa_fwd_fp8")
+            if events is not None:
+                events[1].record(stream)
+            return
         if drop:
             st = fa.fa_fwd_dropout(q, k, v, o, lse, fwd_ws, w.scale, w.causal, args.dropout, seed,
                                    0, stream)
@@ -293,9 +314,10 @@ def main():
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
     out = {
-        "metric": (METRIC if args.workload == "c3" and not drop
+        "metric": (METRIC if args.workload == "c3" and not drop and not fp8
                    else f"attention throughput, {args.workload}"
-                   + (f" with dropout p={args.dropout}" if drop else "")),
+                   + (f" with dropout p={args.dropout}" if drop else "")
+                   + (" FP8 (E4M3) forward" if fp8 else "")),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -303,14 +325,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8 e4m3 (bf16 out)" if fp8 else w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to the storage dtype",
         "config": {"workload": f"{'causal' if w.causal else 'non-causal'} attention "
                                f"{'forward+backward' if bwd else 'forward'} B={w.B} Hq={w.Hq} "
                                f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}"
                                + (" over a paged K/V cache (128-key pages, shuffled pool)"
                                   if paged else "")
-                               + (f" with dropout p={args.dropout} on P" if drop else ""),
+                               + (f" with dropout p={args.dropout} on P" if drop else "")
+                               + (" as E4M3 inputs, P rounded to E4M3, bf16 output" if fp8 else ""),
                    "name": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N_q": w.Nq,
                    "N_kv": w.Nkv, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
@@ -329,10 +352,11 @@ def main():
     else:
         tflops = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
         fwd_t = fwd_flop / (per_kernel_ms["fwd"] * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
         out.update({"value": round(tflops, 2), "unit": "TFLOP/s",
-                    "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                    "pct_peak": round(100 * tflops / peak, 2),
                     "fwd_tflops": round(fwd_t, 2),
-                    "fwd_pct_peak": round(100 * fwd_t / PEAK_BF16_TFLOPS, 2)})
+                    "fwd_pct_peak": round(100 * fwd_t / peak, 2)})
         flop = {"fwd": fwd_flop}
         if bwd and drop:
             bwd_t = bwd_flop / (per_kernel_ms["bwd"] * 1e-3) / 1e12
@@ -343,15 +367,15 @@ def main():
             bwd_t = bwd_flop / (bwd_ms * 1e-3) / 1e12
             out.update({"bwd_tflops": round(bwd_t, 2), "bwd_pct_peak": round(100 * bwd_t / PEAK_BF16_TFLOPS, 2)})
             flop.update({"bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop})
-        on_profiled = args.workload == "c3" and not drop
+        on_profiled = args.workload == "c3" and not drop and not fp8
         lines = {kname: mfma_roofline(kname, f, per_kernel_ms[kname],
-                                      read_traffic(kname) if on_profiled else None)
+                                      read_traffic(kname) if on_profiled else None, peak)
                  for kname, f in flop.items()}
         # The dominant kernel is the one with the longest average launch.
         dom = max(lines, key=lambda kname: per_kernel_ms[kname])
         out["roofline"] = lines[dom]
         out["roofline_all"] = lines
-    if not args.no_cpu_baseline and not drop:
+    if not args.no_cpu_baseline and not drop and not fp8:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0

@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dropout.argtypes = bwd[:-2] + [f, u64, u64, i, vp]
     lib.fa_bwd_dropout.restype = i
     lib.fa_dropout_mask.argtypes = [vp, i, i, i, i, f, u64, u64, vp]
+    lib.fa_fwd_fp8.argtypes = [vp] * 5 + shape + [f, i, f, f, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_dropout_mask.restype = i
     _lib = lib
     return lib
@@ -324,3 +326,37 @@ def dropout_mask(B: int, Hq: int, Nq: int, Nkv: int, dropout_p: float, seed: int
     if st != FA_OK:
         raise FAError(st, "fa_dropout_mask")
     return keep
+
+
+# ---------------------------------------------------------------------- fp8
+
+_FP8_TYPES = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool, descale_q: float = 1.0,
+               descale_k: float = 1.0, descale_v: float = 1.0, stream=None) -> int:
+    """Call fa_fwd_fp8 (E4M3 codes as uint8 or float8_e4m3fn tensors, o bf16);
+    returns the status code (no exception)."""
+    for name, t in {"q8": q8, "k8": k8, "v8": v8}.items():
+        _check({name: t})
+        if t.dtype not in _FP8_TYPES:
+            raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), not {t.dtype}")
+    _check({"o": o}, torch.bfloat16)
+    _check({"lse": lse}, torch.float32)
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q8, k8)
+    return load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                             Nkv, d, float(scale), int(bool(causal)), float(descale_q),
+                             float(descale_k), float(descale_v), _stream(stream))
+
+
+def forward_fp8(q8, k8, v8, descale_q: float = 1.0, descale_k: float = 1.0, descale_v: float = 1.0,
+                causal: bool = False, scale: float | None = None, stream=None):
+    """O (bf16), LSE of attention over E4M3 inputs (see fa_fwd_fp8 in fa.h)."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q8, k8)
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    st = fa_fwd_fp8(q8, k8, v8, o, lse, _default_scale(d, scale), causal, descale_q, descale_k,
+                    descale_v, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
+    return o, lse

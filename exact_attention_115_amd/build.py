@@ -29,6 +29,7 @@ SOURCES = [
     "fa_bwd.hip",
     "fa_bwd_dq.hip",
     "fa_dropout.hip",
+    "fa_fwd_fp8.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -402,6 +402,38 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   return FA_OK;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nkv, int d, float scale, int causal, float descale_q,
+               float descale_k, float descale_v, hipStream_t stream) {
+  bool empty = false;
+  int st = check_shape(B, Hq, Hkv, Nq, Nkv, d, FA_BF16, &empty);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  st = check_scale(scale, causal);
+  if (st != FA_OK) return st;
+  const float ds[3] = {descale_q, descale_k, descale_v};
+  for (float x : ds)
+    if (!(x > 0.0f) || !isfinite(x)) return FA_ERR_SCALE;
+  if (empty) return FA_OK;
+  Problem p = make_problem(B, Hq, Hkv, Nq, Nkv, d, scale, causal, FA_BF16);
+  const size_t qb = (size_t)B * Hq * Nq * d;   // one byte per element
+  const size_t kb = (size_t)B * Hkv * Nkv * d;
+  const size_t ob = 2 * qb;                    // bf16 output
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  if (!q || !o || !lse) return FA_ERR_NULLPTR;
+  if (kb > 0 && (!k || !v)) return FA_ERR_NULLPTR;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 16)) return FA_ERR_ALIGNMENT;
+  if (kb > 0 && (!aligned(k, 16) || !aligned(v, 16))) return FA_ERR_ALIGNMENT;
+  const Range in[3] = {range_of(q, qb), range_of(k, kb), range_of(v, kb)};
+  const Range out[2] = {range_of(o, ob), range_of(lse, lb)};
+  for (const Range& a : out)
+    for (const Range& b : in)
+      if (overlap(a, b)) return FA_ERR_OVERLAP;
+  if (overlap(out[0], out[1])) return FA_ERR_OVERLAP;
+  Fp8Ptrs t{q, k, v, o, lse, descale_q, descale_k, descale_v};
+  return to_status(launch_fwd_fp8(p, t, stream));
+}
+
 int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float dropout_p,
                     uint64_t seed, uint64_t offset, hipStream_t stream) {
   if (B < 0 || Hq < 0 || Nq < 0 || Nkv < 0) return FA_ERR_SHAPE;

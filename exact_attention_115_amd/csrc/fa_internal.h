@@ -37,6 +37,17 @@ struct PagedPtrs {
   int page_size, max_pages, num_pages;
 };
 
+// FP8 forward: E4M3 codes for q, k, v with per-tensor descale factors
+// (real value = code value * descale); o is bf16.
+struct Fp8Ptrs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float descale_q, descale_k, descale_v;
+};
+
 struct BwdPtrs {
   const void* q;
   const void* k;
@@ -75,6 +86,7 @@ hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream
 hipError_t launch_fwd_mfma(const Problem& p, const FwdPtrs& t, hipStream_t stream,
                            const DropParams* drop = nullptr);
 hipError_t launch_decode(const Problem& p, const FwdPtrs& t, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Problem& p, const Fp8Ptrs& t, hipStream_t stream);
 hipError_t launch_decode_paged(const Problem& p, const FwdPtrs& t, const PagedPtrs& pg,
                                hipStream_t stream);
 hipError_t launch_dropout_mask(uint8_t* keep, int B, int Hq, int Nq, int Nkv, const DropParams& dp,

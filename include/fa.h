@@ -206,6 +206,24 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
 int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float dropout_p,
                     uint64_t seed, uint64_t offset, hipStream_t stream);
 
+/* FP8 forward ([KB] §07 notes an FP8 path of the same algorithm on Hopper):
+ * q [B, Hq, N_q, 128], k, v [B, Hkv, N_kv, 128] hold OCP E4M3 codes (1 byte
+ * each: sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+ * 448; 0x7F, 0xFF are NaN) whose real values are code value * descale_q
+ * (descale_k, descale_v). Computes the attention of those real values with
+ * scale and causal as in fa_fwd, using E4M3 operands on the matrix cores for
+ * S = Q K^T and for P V, where the probabilities (each taken relative to a
+ * running row maximum, so at most 256) are rounded to E4M3 nearest-even;
+ * the softmax state and all sums are float32. Writes o [B, Hq, N_q, 128] as
+ * bf16 and lse [B, Hq, N_q] float32 (natural log). Head dim 128 only
+ * (FA_ERR_UNSUPPORTED otherwise); descale factors finite and > 0 (else
+ * FA_ERR_SCALE). No workspace. Alignment, aliasing, status codes and
+ * execution as fa_fwd. */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+               float scale, int causal, float descale_q, float descale_k, float descale_v,
+               hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -240,3 +240,26 @@ def test_bwd_dropout_rejects_bad_arguments():
     assert call(ws=None) == -1
     assert call(dq=P(1)) == -8
     assert call(B=0) == 0
+
+
+def test_fwd_fp8_rejects_bad_arguments():
+    lib = fa.load()
+
+    def call(**kw):
+        a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=128,
+                 scale=0.1, causal=0, dq=1.0, dk=1.0, dv=1.0)
+        a.update(kw)
+        return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], a["dq"], a["dk"],
+                              a["dv"], None)
+
+    assert call(d=64) == -3
+    assert call(d=96) == -3
+    for x in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(dq=x) == -6 and call(dk=x) == -6 and call(dv=x) == -6
+    assert call(scale=0.0) == -6
+    assert call(q=None) == -1
+    assert call(Hq=3, Hkv=2) == -2
+    assert call(q=P(1, 8)) == -4
+    assert call(o=P(1)) == -8
+    assert call(Nq=0) == 0

@@ -1,0 +1,104 @@
+"""GPU parity of the FP8 (E4M3) forward (fa_fwd_fp8) against the float64
+oracle in oracle/fp8.py.
+
+The oracle is the definition on the decoded inputs; the kernel also rounds
+the probabilities to E4M3 for the P V product. The bar per output element is
+the oracle's bound for that rounding (oracle.fp8.p_rounding_bound: each
+normalised weight moves by at most max(2^-4 P, 2^-10)) plus the bf16 rounding
+of O (2^-8 |O|, twice its half-unit) and 1e-4 for float32 sums. LSE is taken
+from the unrounded probabilities: 1e-3, as for the 16-bit forward.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_115_amd as fa
+from oracle import fp8 as f8
+from parity_util import say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def e4m3_inputs(B, Hq, Hkv, Nq, Nkv, seed, descales=(0.5, 0.25, 2.0)):
+    """E4M3 codes of N(0, 1) draws divided by each tensor's descale factor."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    dq, dk, dv = descales
+    q = (torch.randn((B, Hq, Nq, 128), generator=g) / dq).to(torch.float8_e4m3fn)
+    k = (torch.randn((B, Hkv, Nkv, 128), generator=g) / dk).to(torch.float8_e4m3fn)
+    v = (torch.randn((B, Hkv, Nkv, 128), generator=g) / dv).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), k.view(torch.uint8), v.view(torch.uint8)
+
+
+def check_fp8(o, lse, q8, k8, v8, heads, causal, scale, descales, label):
+    G = q8.shape[1] // k8.shape[1]
+    dq, dk, dv = descales
+    worst = 0.0
+    for b, h in heads:
+        qq, kk, vv = (x.numpy() for x in (q8[b, h], k8[b, h // G], v8[b, h // G]))
+        o_ref, lse_ref = f8.head_forward_fp8(qq, kk, vv, causal, scale, dq, dk, dv)
+        bound = f8.p_rounding_bound(qq, kk, vv, causal, scale, dq, dk, dv)
+        og = to_f64(o[b, h])
+        lg = to_f64(lse[b, h])
+        assert np.all(np.isfinite(og))
+        err = np.abs(og - o_ref)
+        allowed = bound + 2.0 ** -8 * np.abs(o_ref) + 1e-4
+        worst = max(worst, float(np.max(err / allowed)))
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lg), fin)
+        lerr = float(np.max(np.abs(lg[fin] - lse_ref[fin]))) if fin.any() else 0.0
+        say(f"  [{label} head {b},{h}] O max-abs {err.max():.3e} (max |O| {np.abs(o_ref).max():.2f}), "
+            f"worst err/bound {float(np.max(err / allowed)):.3f}, LSE max-abs {lerr:.3e}")
+        assert np.all(err <= allowed), float(np.max(err / allowed))
+        assert lerr <= 1e-3
+    return worst
+
+
+CASES = [
+    # B, Hq, Hkv, Nq, Nkv, causal
+    (1, 4, 2, 200, 300, True),
+    (2, 8, 8, 1000, 1000, False),
+    (1, 2, 1, 1, 700, False),
+    (1, 2, 2, 130, 70, True),       # N_q > N_kv: the first rows see no key
+    (3, 6, 3, 65, 129, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_fp8_forward_parity(case):
+    B, Hq, Hkv, Nq, Nkv, causal = case
+    scale = 1.0 / np.sqrt(128)
+    descales = (0.5, 0.25, 2.0)
+    say(f"fp8 forward {case}")
+    q8, k8, v8 = e4m3_inputs(B, Hq, Hkv, Nq, Nkv, seed=101 + Nq, descales=descales)
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *descales, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    heads = sorted({(0, 0), (B - 1, Hq - 1), (B // 2, Hq // 2)})
+    check_fp8(o.cpu(), lse.cpu(), q8, k8, v8, heads, causal, scale, descales, str(case))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_forward_long_sampled(causal):
+    """256-row workgroups (N_q >= 4096 and enough tiles to fill the GPU) with a
+    ragged tail; two sampled heads."""
+    B, Hq, Hkv, N = 1, 16, 16, 4100
+    scale = 1.0 / np.sqrt(128)
+    descales = (1.0, 1.0, 1.0)
+    q8, k8, v8 = e4m3_inputs(B, Hq, Hkv, N, N, seed=111, descales=descales)
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *descales, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    check_fp8(o.cpu(), lse.cpu(), q8, k8, v8, [(0, 0), (0, Hq - 1)], causal, scale, descales,
+              f"long causal={causal}")
+
+
+def test_fp8_forward_no_keys_and_repeatable():
+    q8, k8, v8 = e4m3_inputs(1, 2, 2, 40, 64, seed=113)
+    qg, kg, vg = q8.cuda(), k8.cuda(), v8.cuda()
+    o1, l1 = fa.forward_fp8(qg, kg, vg, 0.5, 0.25, 2.0, causal=True)
+    o2, l2 = fa.forward_fp8(qg, kg, vg, 0.5, 0.25, 2.0, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    empty = torch.empty((1, 2, 0, 128), dtype=torch.uint8, device="cuda")
+    o3, l3 = fa.forward_fp8(qg, empty, empty, causal=False)
+    torch.cuda.synchronize()
+    assert bool((o3 == 0).all()) and bool(torch.isneginf(l3).all())
