@@ -1,24 +1,20 @@
-// K / V tile staging for the forward and decode kernels: a tile of BC = 64
-// keys is read from global memory with 16-byte buffer loads into registers,
-// then written to LDS row-major, K[key][dim] and V[key][dim], with padded
-// rows so that the matrix-core operand reads below do not hit the same LDS
-// bank twice in one access group:
-// * K rows are read 16 bytes per lane, 16 consecutive rows per access
-//   group; a 16-byte pad puts consecutive rows 4 banks apart, so the 16 rows
-//   cover all 64 banks once.
+// K / V tile staging for the 16-bit forward, decode and backward kernels: a
+// tile of BC = 64 keys (or query rows) is copied from global memory straight
+// into LDS by buffer loads with an LDS destination (no register staging), in
+// blocked layouts chosen so that the matrix-core operand reads are free of
+// LDS bank conflicts:
+// * K rows are read 16 bytes per lane, 16 consecutive rows per access group
+//   (the A operand of S^T = K Q^T);
 // * V is consumed as the A operand of O^T += V^T P^T, i.e. eight consecutive
-//   KEYS of one dim per lane, which is a column of the row-major tile.
-//   gfx950's transposed LDS read (ds_read_b64_tr_b16) delivers exactly that:
-//   within each group of 16 lanes, the lanes' 4-element row chunks form a
-//   16 x 4 matrix M (row = source lane) and result lane i receives
-//   M[4k + i/4][i % 4], k = 0..3. One such group reads 32 bytes from each of
-//   4 consecutive rows; a 32-byte pad puts those rows 8 banks apart.
-//   vt_addr() gives each lane the row chunk to point at so that lane (h, c)
-//   receives V[key0 + 8h + 4s + k][dim0 + c], k = 0..3, for half s = 0, 1.
-//
-// Global reads go through a buffer resource whose size is the head's K (or
-// V) extent: reads past the last key return zero without a branch, and the
-// caller masks those keys to -inf.
+//   KEYS of one dim per lane, a column of the row-major tile. gfx950's
+//   transposed LDS read (ds_read_b64_tr_b16) delivers exactly that: within
+//   each group of 16 lanes, the lanes' 4-element row chunks form a 16 x 4
+//   matrix M (row = source lane) and result lane i receives M[4k + i/4][i % 4],
+//   k = 0..3.
+// The layouts and the per-lane read offsets are below (DmaTile, k_read_base,
+// v_read_base, kt_read_base). Global reads go through a buffer resource whose
+// size is the head's K (or V) extent: reads past the last key return zero
+// without a branch, and the caller masks those keys to -inf.
 #pragma once
 
 #include "fa_device.h"
@@ -26,89 +22,14 @@
 namespace fa {
 
 constexpr int BC = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup that stage a tile
+constexpr int NT = 256;  // threads per decode workgroup
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct KVTileLds {
-  static constexpr int RSK = D + 8;   // K row stride (elements)
-  static constexpr int RSV = D + 16;  // V row stride (elements)
-  static constexpr int K_ELEMS = BC * RSK;
-  static constexpr int V_ELEMS = BC * RSV;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-};
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled; reads at or
 // past `bytes` return zero).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ inline u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-// Global loads of one K/V tile held in registers between issue and LDS write.
-template <int D>
-struct KVTileRegs {
-  static constexpr int CH = (BC * D / 8) / NT;  // 16-byte chunks per thread, per tensor
-  u32x4 k[CH];
-  u32x4 v[CH];
-};
-
-// Byte offset, inside a head, of chunk i of thread tid for the tile at key 0
-// (add key0 * D * 2 for the tile at key0); also the chunk's LDS position.
-template <int D>
-__device__ inline uint32_t tile_chunk_off(int tid, int i) {
-  const int id = tid + NT * i;
-  return (uint32_t)((id / (D / 8)) * D + (id % (D / 8)) * 8) * 2u;
-}
-
-template <int D>
-__device__ inline void load_k_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t kr, int key0, int tid) {
-  const uint32_t base = (uint32_t)key0 * D * 2u;
-#pragma unroll
-  for (int i = 0; i < KVTileRegs<D>::CH; ++i) r.k[i] = buf_ld16(kr, base + tile_chunk_off<D>(tid, i));
-}
-
-template <int D>
-__device__ inline void load_v_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t vr, int key0, int tid) {
-  const uint32_t base = (uint32_t)key0 * D * 2u;
-#pragma unroll
-  for (int i = 0; i < KVTileRegs<D>::CH; ++i) r.v[i] = buf_ld16(vr, base + tile_chunk_off<D>(tid, i));
-}
-
-// K tile at key k0 and V tile at key v0.
-template <int D>
-__device__ inline void load_kv_tile(KVTileRegs<D>& r, __amdgpu_buffer_rsrc_t kr,
-                                    __amdgpu_buffer_rsrc_t vr, int k0, int v0, int tid) {
-  load_k_tile<D>(r, kr, k0, tid);
-  load_v_tile<D>(r, vr, v0, tid);
-}
-
-template <int D>
-__device__ inline void store_k_tile(const KVTileRegs<D>& r, uint16_t* ks, int tid) {
-#pragma unroll
-  for (int i = 0; i < KVTileRegs<D>::CH; ++i) {
-    const int id = tid + NT * i;
-    *reinterpret_cast<u32x4*>(ks + (id / (D / 8)) * KVTileLds<D>::RSK + (id % (D / 8)) * 8) = r.k[i];
-  }
-}
-
-template <int D>
-__device__ inline void store_v_tile(const KVTileRegs<D>& r, uint16_t* vs, int tid) {
-#pragma unroll
-  for (int i = 0; i < KVTileRegs<D>::CH; ++i) {
-    const int id = tid + NT * i;
-    *reinterpret_cast<u32x4*>(vs + (id / (D / 8)) * KVTileLds<D>::RSV + (id % (D / 8)) * 8) = r.v[i];
-  }
-}
-
-template <int D>
-__device__ inline void store_kv_tile(const KVTileRegs<D>& r, uint16_t* ks, uint16_t* vs, int tid) {
-  store_k_tile<D>(r, ks, tid);
-  store_v_tile<D>(r, vs, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,33 +138,9 @@ __device__ inline uint32_t v_read_base(int h, int c) {
   return (uint32_t)(8 * h * T::RB + (j >> 2) * 64 + (2 * (c >> 4) + ((j >> 1) & 1)) * 16 + 8 * (j & 1));
 }
 
-// Element offset, inside a V tile, of the 4-element row chunk lane (h, c)
-// points at so that the transposed read returns V[key0 + 8h + 4s + k][dim0 + c]
-// (k = 0..3). Lane (h, c) sits in 16-lane group 2h + c/16 at position
-// j = c % 16; it supplies row key0 + 8h + 4s + j/4, columns
-// dim0 + 16 (c/16) + 4 (j % 4) .. +3.
-template <int RS>
-__device__ inline int vt_addr(int h, int c, int key0, int dim0, int s) {
-  const int j = c & 15;
-  return (key0 + 8 * h + 4 * s + (j >> 2)) * RS + dim0 + 16 * (c >> 4) + 4 * (j & 3);
-}
-
 __device__ inline s16x4 ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
-}
-
-// The A operand V^T[dim0 + c][key0 + 8h .. +7] from the row-major V tile.
-template <typename T, int RS>
-__device__ inline typename T::vec8 load_vt_operand(const uint16_t* vs, int h, int c, int key0,
-                                                   int dim0) {
-  const s16x4 lo = ds_read_tr16(vs + vt_addr<RS>(h, c, key0, dim0, 0));
-  const s16x4 hi = ds_read_tr16(vs + vt_addr<RS>(h, c, key0, dim0, 1));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 x;
-  x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
-  x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
-  return __builtin_bit_cast(typename T::vec8, x);
 }
 
 // The A operand V^T[dim0 + c][key0 + 8h .. +7] (dim0 = 32 od, key0 = 16 ch)
