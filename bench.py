@@ -52,11 +52,14 @@ KERNEL_SOURCES = {
     "bwd_pre": ["fa_bwd.hip"] + COMMON,
     "bwd_dkdv": ["fa_bwd.hip"] + COMMON,
     "bwd_dq": ["fa_bwd_dq.hip"] + COMMON,
+    "decode": ["fa_decode.hip"] + COMMON,
 }
 TRAFFIC_SUMMARY = {
     "fwd": "fwd_causal_b1h32n4096d128_bf16_hbm_traffic.md",
     "bwd_dkdv": "bwd_dkdv_causal_b1h32n4096d128_bf16_hbm_traffic.md",
     "bwd_dq": "bwd_dq_causal_b1h32n4096d128_bf16_hbm_traffic.md",
+    # split + combine kernels of one decode call, B=16 Hq=32 Hkv=8 N_kv=8192 d=128
+    "decode": "decode_b16h32kv8n8192d128_bf16_hbm_traffic.md",
 }
 
 
@@ -346,7 +349,8 @@ def main():
         out.update({"value": round(gbs, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                     "cache": "cold (1 GiB write before each timed call)" if cold else "warm"})
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                           "traffic": read_traffic("decode") if args.workload == "c5dg" else None,
                            "kernel": "decode split + combine (one fa_fwd" + ("_paged" if paged else "") + " call)",
                            "algorithmic_bytes": nbytes}
     else:

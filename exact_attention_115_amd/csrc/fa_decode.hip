@@ -47,6 +47,13 @@ struct DecArgs {
 // at dst + (wave * blocks + i) KiB, 16 bytes per lane. Issued from inline
 // assembly so that the compiler adds no waits of its own for them: the
 // caller waits on vmcnt before the barrier that precedes any read.
+//
+// Decode reads every byte of Q, K and V exactly once, so these copies are
+// non-temporal (`nt`): the lines they bring in are not kept in the caches.
+// With ordinary loads the stream displaces whatever the caches hold, and
+// when that is data written by earlier work (dirty lines) every displaced
+// line costs an extra write to HBM: on a cache full of such lines that
+// halves the decode's read rate.
 __device__ __forceinline__ void copy_blocks_async(uint8_t* dst, const void* base, uint32_t bytes,
                                                   uint32_t src, int wave, int lane, int blocks) {
   for (int i = 0; i < blocks; ++i) {
@@ -63,7 +70,7 @@ __device__ __forceinline__ void copy_blocks_async(uint8_t* dst, const void* base
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
         :
         : "s"(lds), "v"((uint32_t)lane * 16u), "s"(rsrc)
         : "memory", "m0");
@@ -92,7 +99,7 @@ __device__ __forceinline__ void copy_tile_async(uint8_t* tile, const uint16_t* h
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
         :
         : "s"(lds), "v"(lane_src), "s"(rsrc)
         : "memory", "m0");
