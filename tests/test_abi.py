@@ -117,6 +117,20 @@ def test_fwd_rejects_bad_arguments():
     assert fwd(lse=P(4, 1024)) == -8  # lse inside o
 
 
+def test_size_limits_are_enforced():
+    """One head's K (or V) is addressed with 32-bit byte offsets: the calls
+    accept N_kv * d * 4 < 2^31 (N_kv <= 4194303 at d = 128, 8388607 at
+    d = 64) and B * Hq * N_q, B * Hkv * N_kv < 2^31; beyond that they return
+    FA_ERR_UNSUPPORTED before touching any pointer."""
+    assert fwd(Nkv=(1 << 31) // (128 * 4), d=128) == -3
+    assert fwd(Nkv=(1 << 31) // (64 * 4), d=64) == -3
+    assert fwd(Nq=1, Nkv=(1 << 31) // (128 * 4), d=128, ws=P(10), ws_bytes=1 << 30) == -3
+    assert fwd(B=1, Hq=2, Hkv=2, Nq=1 << 30) == -3
+    assert fwd(B=2, Hq=2, Hkv=1, Nkv=1 << 30) == -3
+    assert bwd(Nkv=(1 << 31) // (128 * 4), d=128) == -3
+    assert bwd(B=1, Hq=2, Hkv=2, Nq=1 << 30) == -3
+
+
 def test_fwd_decode_needs_workspace():
     assert fwd(Nq=1, Nkv=8192, ws=None) == -1
     need = fa.load().fa_fwd_workspace_size(1, 2, 2, 1, 8192, 64, fa.FA_BF16)
