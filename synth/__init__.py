@@ -109,3 +109,38 @@ def random_tensors(shape_q, shape_kv, dtype: str, seed: int, with_grad: bool = F
 def to_f64(t):
     """Widen a CPU tensor to a float64 numpy array (exact for f32/bf16/f16)."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def ramp_tensors(shape_q, shape_kv, dtype: str, seed: int, ramp: str, peak: float = 32.0,
+                 with_grad: bool = False):
+    """Score-range stress inputs: q and k drawn as |N(0, 1)| (so every score
+    q . k is positive and grows with the size of k), each key row j of k
+    multiplied by a factor r_j that varies along the sequence, v and dO as
+    N(0, 1). ``ramp`` picks r_j for N_kv keys:
+
+    * "up":   r_j = 1 + (peak - 1) j / (N_kv - 1), each later key tile scores higher;
+    * "down": the reverse, the first tile holds every row's maximum;
+    * "wave": r_j = 1 + (peak - 1) (1 + sin(j / 40)) / 2, maxima come and go.
+
+    Same generator recipe as :func:`random_tensors` (q, k, v, dO in that order),
+    rounded to the storage dtype at the end.
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    dt = _DTYPES[dtype]
+    q = torch.randn(shape_q, generator=g, dtype=torch.float32).abs()
+    k = torch.randn(shape_kv, generator=g, dtype=torch.float32).abs()
+    v = torch.randn(shape_kv, generator=g, dtype=torch.float32)
+    do = torch.randn(shape_q, generator=g, dtype=torch.float32) if with_grad else None
+    n = shape_kv[-2]
+    j = torch.arange(n, dtype=torch.float32)
+    t = j / max(n - 1, 1)
+    if ramp == "up":
+        r = 1.0 + (peak - 1.0) * t
+    elif ramp == "down":
+        r = 1.0 + (peak - 1.0) * (1.0 - t)
+    elif ramp == "wave":
+        r = 1.0 + (peak - 1.0) * 0.5 * (1.0 + torch.sin(j / 40.0))
+    else:
+        raise ValueError(ramp)
+    k = k * r[:, None]
+    return q.to(dt), k.to(dt), v.to(dt), (do.to(dt) if do is not None else None)
