@@ -102,3 +102,43 @@ def test_fp8_forward_no_keys_and_repeatable():
     o3, l3 = fa.forward_fp8(qg, empty, empty, causal=False)
     torch.cuda.synchronize()
     assert bool((o3 == 0).all()) and bool(torch.isneginf(l3).all())
+
+
+RAMP_CASES = [
+    # B, Hq, Hkv, Nq, Nkv, causal
+    (1, 4, 2, 300, 700, True),
+    (2, 2, 1, 1, 2000, False),
+]
+
+
+@pytest.mark.parametrize("ramp", ["up", "down", "wave"])
+@pytest.mark.parametrize("case", RAMP_CASES, ids=[str(c) for c in RAMP_CASES])
+def test_fp8_forward_under_score_ramps(case, ramp):
+    """The online-softmax rescale of the FP8 kernel: key rows scaled by a
+    factor rising, falling or oscillating along the sequence (see
+    tests/test_parity_rescale.py), quantised to E4M3 with descale factors 1.
+
+    Peak factor 6: scores reach about 45 natural-log units and, for "up",
+    each 64-key tile raises the maximum by about 3 units, past the kernel's
+    rescale threshold (a lane's tile sum above 256) on most tiles. The
+    16-bit tests go to 250 units; here that would test the matrix cores'
+    8-bit accumulation instead: the 32x32x64 E4M3 product does not sum its
+    64 terms exactly in float32 (on random E4M3 operands its error reaches
+    2^-12.9 of the sum of the terms' magnitudes, against 2^-21 for a float32
+    running sum), so the scores themselves move by up to ~2^-13 of
+    scale * sum_c |q_c k_c|, which is ~3e-3 at 250 units, more than the LSE
+    bar, while at 45 units it stays near 5e-4."""
+    from synth import ramp_tensors
+
+    B, Hq, Hkv, Nq, Nkv, causal = case
+    scale = 1.0 / np.sqrt(128)
+    descales = (1.0, 1.0, 1.0)
+    say(f"fp8 ramp {ramp} {case}")
+    q, k, v, _ = ramp_tensors((B, Hq, Nq, 128), (B, Hkv, Nkv, 128), "f32", seed=121 + Nq,
+                              ramp=ramp, peak=6.0)
+    assert float(k.abs().max()) < 448.0
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn).view(torch.uint8) for x in (q, k, v))
+    o, lse = fa.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), *descales, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    heads = sorted({(0, 0), (B - 1, Hq - 1)})
+    check_fp8(o.cpu(), lse.cpu(), q8, k8, v8, heads, causal, scale, descales, f"{ramp} {case}")
