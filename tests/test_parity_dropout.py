@@ -195,3 +195,28 @@ def test_backward_dropout_long_sampled():
             rel = float(np.linalg.norm(to_f64(g) - ref) / np.linalg.norm(ref))
             say(f"  [long head {h}] {name} Frobenius rel {rel:.3e}")
             assert rel <= TOL[w.dtype]["grad_rel"], (h, name, rel)
+
+
+@pytest.mark.parametrize("ramp", ["up", "wave"])
+def test_dropout_under_score_ramps(ramp):
+    """The rescale of the online softmax with dropout on: key rows scaled by a
+    factor rising or oscillating along the sequence (scores to about 250
+    natural-log units, a new maximum on every tile for "up"; see
+    tests/test_parity_rescale.py); forward and backward against the oracle."""
+    from synth import ramp_tensors
+
+    B, Hq, Hkv, Nq, Nkv, d, causal, dtype, p = 1, 4, 2, 300, 500, 128, True, "bf16", 0.3
+    scale = 1.0 / np.sqrt(d)
+    seed, offset = 77 + len(ramp), 4
+    say(f"dropout ramp {ramp}")
+    q, k, v, do = ramp_tensors((B, Hq, Nq, d), (B, Hkv, Nkv, d), dtype, seed=83, ramp=ramp,
+                               peak=32.0, with_grad=True)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = fa.forward_dropout(qg, kg, vg, p, seed, offset, causal=causal, scale=scale)
+    grads = fa.backward_dropout(qg, kg, vg, o, lse, dog, p, seed, offset, causal=causal,
+                                scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = drop.attention_forward_dropout(to_f64(q), to_f64(k), to_f64(v), causal, scale,
+                                                    f32(p), seed, offset)
+    check_dropout_forward(o, lse, o_ref, lse_ref, dtype, p, f"ramp {ramp}")
+    check_dropout_grads(grads, q, k, v, do, causal, scale, p, seed, offset, dtype, f"ramp {ramp}")
