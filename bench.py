@@ -17,6 +17,12 @@ of two N x d operands (S, dP, dV, dK, dQ) split as four in the key-block
 kernel and one (dQ = dS K) in the query-tile kernel; the S and dP that the
 query-tile kernel recomputes are an implementation cost and are not counted.
 
+Warm-up: the GPU reaches its steady clock only after some tens of
+milliseconds under load; at the default workload the first ~50 steps run up
+to ~15 % slower than the later ones. The default of 100 untimed warm-up
+steps (about 70 ms) therefore precedes the 50 timed ones; ``--warmup`` and
+``--steps`` override both.
+
 Prints ONE JSON line. ``--workload`` selects another synthetic workload for
 development measurements (decode workloads report HBM GB/s, each timed call
 starting from cold caches unless --warm-cache).
@@ -66,8 +72,8 @@ TRAFFIC_SUMMARY = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
