@@ -91,10 +91,38 @@ def parse():
     return ap.parse_args()
 
 
+def code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that the hash below changes with the code but not with its comments.
+    String and character literals are kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(kernel_key):
+    """sha256 (first 16 hex digits) of the code, comments aside, of the
+    files the kernel is built from."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel_key]:
-        h.update(open(os.path.join(CSRC, name), "rb").read())
+        h.update(code_only(open(os.path.join(CSRC, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,9 +17,9 @@
 //             the block stay in registers; the workgroup loops over the query
 //             heads of the group (GQA/MQA: dK, dV summed in registers, no
 //             atomics) and over the 64-row query tiles that can see the block
-//             (causal: only tiles at or below the diagonal). Q / dO tiles are
-//             double-buffered in LDS, the next one loading while the current
-//             one is used. Per tile:
+//             (causal: only tiles at or below the diagonal). Q / dO tiles go
+//             through a ring of four LDS slots, loaded two tiles ahead of
+//             their use. Per tile:
 //               S = Q K^T and dP = dO V^T  (lane = key, 16 query rows / lane)
 //               P, dS in registers
 //               dV^T += dO^T P,  dK^T += Q^T dS   (accumulated in registers;

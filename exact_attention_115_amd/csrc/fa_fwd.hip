@@ -2,7 +2,7 @@
 //
 // Method ([BLOG] "AI infra. 一层全看懂(五)Flash Attention" §五; [KB]
 // "FlashAttention：为什么少搬数据，反而算得更快" §03-§04): one workgroup per
-// tile of 128 query rows (the outer loop); it walks the key/value tiles of 64
+// tile of 256 or 128 query rows (the outer loop); it walks the key/value tiles of 64
 // rows its rows may see (the inner loop). Each score tile S = Q K^T is
 // produced on chip, scaled, masked and folded at once into per-row online
 // softmax state -- m (running maximum), l (running sum of exp(s - m)) and the
@@ -11,11 +11,12 @@
 // chip, so no N x N matrix is ever written to memory.
 //
 // gfx950 mapping:
-// * 4 waves per workgroup, 32 query rows per wave. The score tile is computed
-//   transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: the query index is the
-//   matrix-core column, so every lane owns ONE query row (half of its keys in
-//   each half-wave) and the row max / row sum need only lane-local work plus
-//   one exchange between the two half-waves.
+// * 8 or 4 waves per workgroup (two waves per SIMD either way: one 8-wave
+//   workgroup or two 4-wave ones per CU), 32 query rows per wave. The score
+//   tile is computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16: the
+//   query index is the matrix-core column, so every lane owns ONE query row
+//   (half of its keys in each half-wave) and the row max / row sum need only
+//   lane-local work plus one exchange between the two half-waves.
 // * K rows are fed to the matrix core in the order row_perm() gives, which
 //   leaves each lane's accumulators holding runs of 8 consecutive keys: they
 //   are, unchanged, the B operand (P^T) of O^T += V^T P^T, so P never leaves
@@ -23,11 +24,11 @@
 // * O^T = V^T P^T keeps the output accumulator lane = query as well, so the
 //   per-row rescale is lane-local. V stays row-major in LDS; its transpose is
 //   taken by the gfx950 transposed LDS read (see fa_tile.h).
-// * K and V tiles are double-buffered in LDS, K one tile ahead of V: while
-//   tile j is exponentiated and multiplied by V, the matrix cores already
-//   compute the scores of tile j + 1 (software pipelining inside each wave),
-//   and the global loads of K tile j + 2 and V tile j + 1 are in flight; one
-//   barrier per tile.
+// * K and V tiles are double-buffered in LDS. Each wave runs a three-stage
+//   software pipeline: in step i it multiplies P of tile i by V tile i,
+//   exponentiates the scores of tile i + 1 and computes the scores of tile
+//   i + 2, as one interleaved instruction stream, while the global loads of
+//   K tile i + 3 and V tile i + 1 are in flight; one barrier per tile.
 // * Exponentials use exp2 with log2(e) folded into the scale; the LSE is
 //   converted back to natural-log units at the end.
 // * Few vector-ALU operations per score (the matrix cores outrun them): P is

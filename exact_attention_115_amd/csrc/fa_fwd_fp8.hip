@@ -6,7 +6,9 @@
 // is the forward of fa_fwd.hip ([BLOG] §五 outer loop over query tiles, inner
 // loop over key/value tiles, the online softmax of [KB] §04): per key tile
 // S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (both operands E4M3, float32
-// accumulation), the row state (m, l, U) in float32, P = exp2(S * c - m)
+// results; the product's own sum of 64 terms is coarser than a float32
+// running sum: on random E4M3 operands its error reached 2^-12.9 of the sum
+// of the terms' magnitudes), the row state (m, l, U) in float32, P = exp2(S * c - m)
 // rounded to E4M3 for U += V^T P^T on the same product, and at the end
 // O = descale_v * U / l in bf16 and LSE = m + ln l.
 //
