@@ -198,7 +198,7 @@ def mfma_roofline(kernel, flop, ms, traffic, peak=PEAK_BF16_TFLOPS):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+        print(json.dumps({"error": "this library runs on one GPU only; multi-GPU runs are not "
                                    "implemented (heads would shard across GPUs with no "
                                    "communication)", "n_gpus": args.gpus}))
         return 2
