@@ -188,9 +188,9 @@ int drop_params(float p, uint64_t seed, uint64_t offset, DropParams* out) {
 
 int run_bwd_stage(int stage, const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   switch (stage) {
-    case 0: return to_status(launch_bwd_pre(p, t, stream));
+    case 0: return to_status(launch_bwd_dq_rows(p, t, stream));
     case 1: return to_status(launch_bwd_main(p, t, stream));
-    case 2: return to_status(launch_bwd_dq(p, t, stream));
+    case 2: return to_status(launch_bwd_reduce(p, t, stream));
     default: return FA_ERR_UNSUPPORTED;
   }
 }

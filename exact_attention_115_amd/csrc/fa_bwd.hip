@@ -11,8 +11,11 @@
 // (D_i equals sum_j P_ij dP_ij because O = P V.)
 //
 // Three stages on one stream:
-//   0  pre:   -D_i and -LSE_i / scale for every query row (float32, in the
-//             workspace): the starting values of the dP and S accumulators.
+//   0  dQ:    one workgroup per query tile recomputes P and dS over the key
+//             tiles and keeps dQ in registers (fa_bwd_dq.hip); it also
+//             stores -D_i and -LSE_i / scale for every query row (float32,
+//             in the workspace): the starting values of stage 1's dP and S
+//             accumulators.
 //   1  dK/dV: one workgroup per 128-key block of one (b, kv head). K and V of
 //             the block stay in registers; the workgroup loops over the query
 //             heads of the group (GQA/MQA: dK, dV summed in registers, no
@@ -28,9 +31,7 @@
 //             few key blocks to fill the GPU (e.g. MQA), the query heads of a
 //             group are split over several workgroups, which write float32
 //             partial dK, dV to the workspace instead.
-//   2  dQ:    one workgroup per query tile recomputes P and dS over the key
-//             tiles and keeps dQ in registers (fa_bwd_dq.hip); with a split
-//             head group, also dK = scale * sum of partials, dV = sum.
+//   2  with a split head group only: dK = scale * sum of partials, dV = sum.
 #include <math.h>
 
 #include <type_traits>
@@ -51,56 +52,17 @@ struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* o;
-  const float* lse;
   const uint16_t* dO;
   uint16_t* dk;
   uint16_t* dv;
   const float* lneg;   // -LSE / scale per query row (-inf: row saw no key)
-  float* nd;           // -D per query row
+  const float* nd;     // -D per query row (-D / r with dropout)
   float* dk_part;
   float* dv_part;
   int Hq, Hkv, G, Nq, Nkv, n_kblocks, n_bk, gsplit;
   float scale, scale_log2;
   DropParams drop;  // used only by the dropout instantiations
 };
-
-// ---------------------------------------------------------------- stage 0
-// nd_i = -D_i = -sum_c dO_ic O_ic in float32 (-D_i / r with dropout, r the
-// keep factor), and lneg_i = -LSE_i / scale (-inf for a row that saw no key). Starting the S accumulator of row i at
-// lneg_i and the dP accumulator at nd_i leaves S - LSE / scale and dP - D in
-// them, so P = exp2(scale log2(e) acc) and dS = P acc' need no further
-// per-row terms.
-template <typename T, int D>
-__global__ __launch_bounds__(NTB) void bwd_pre_kernel(const uint16_t* __restrict__ o,
-                                                      const uint16_t* __restrict__ dO,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ nd,
-                                                      float* __restrict__ lneg, size_t rows,
-                                                      float inv_scale, float inv_r) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  constexpr int RPB = NTB / CPR;
-  const int t = threadIdx.x;
-  const size_t row = (size_t)blockIdx.x * RPB + t / CPR;
-  const int ch = t % CPR;
-  float acc = 0.0f;
-  if (row < rows) {
-    const u32x4 a = ld16(o + row * D + ch * 8);
-    const u32x4 g = ld16(dO + row * D + ch * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(T::to_float(a[i] & 0xffffu), T::to_float(g[i] & 0xffffu), acc);
-      acc = fmaf(T::to_float(a[i] >> 16), T::to_float(g[i] >> 16), acc);
-    }
-  }
-#pragma unroll
-  for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && ch == 0) {
-    nd[row] = -acc * inv_r;
-    const float l = lse[row];
-    lneg[row] = l == -INFINITY ? -INFINITY : -l * inv_scale;
-  }
-}
 
 // ---------------------------------------------------------------- stage 1
 // Accumulator start values from a tile's per-row terms x (64 floats in LDS):
@@ -621,8 +583,6 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
   a.q = static_cast<const uint16_t*>(t.q);
   a.k = static_cast<const uint16_t*>(t.k);
   a.v = static_cast<const uint16_t*>(t.v);
-  a.o = static_cast<const uint16_t*>(t.o);
-  a.lse = t.lse;
   a.dO = static_cast<const uint16_t*>(t.dO);
   a.dk = static_cast<uint16_t*>(t.dk);
   a.dv = static_cast<uint16_t*>(t.dv);
@@ -645,18 +605,6 @@ BwdArgs make_args(const Problem& p, const BwdPtrs& t) {
 }
 
 template <typename T, int D>
-hipError_t pre_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
-  const size_t rows = (size_t)p.B * p.Hq * p.Nq;
-  if (rows == 0) return hipSuccess;
-  constexpr int RPB = NTB / (D / 8);
-  dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid, dim3(NTB), 0, stream,
-                     static_cast<const uint16_t*>(t.o), static_cast<const uint16_t*>(t.dO), t.lse,
-                     t.nd, t.lneg, rows, 1.0f / p.scale, t.drop ? 1.0f / t.drop->rscale : 1.0f);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
 hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const BwdArgs a = make_args(p, t);
   if (a.n_kblocks == 0 || a.n_bk == 0) return hipSuccess;
@@ -676,9 +624,7 @@ hipError_t main_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
 }
 
 template <typename T>
-hipError_t dq_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
-  const hipError_t e = launch_bwd_dq_rows(p, t, stream);
-  if (e != hipSuccess) return e;
+hipError_t reduce_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   const int parts = bwd_group_split(p);
   const size_t n4 = (size_t)p.B * p.Hkv * p.Nkv * p.d / 4;
   if (parts > 1 && n4 > 0) {
@@ -693,18 +639,13 @@ hipError_t dq_typed(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
-  if (p.dt == FA_BF16) return p.d == 64 ? pre_typed<BF16, 64>(p, t, stream) : pre_typed<BF16, 128>(p, t, stream);
-  return p.d == 64 ? pre_typed<F16, 64>(p, t, stream) : pre_typed<F16, 128>(p, t, stream);
-}
-
 hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   if (p.dt == FA_BF16) return p.d == 64 ? main_typed<BF16, 64>(p, t, stream) : main_typed<BF16, 128>(p, t, stream);
   return p.d == 64 ? main_typed<F16, 64>(p, t, stream) : main_typed<F16, 128>(p, t, stream);
 }
 
-hipError_t launch_bwd_dq(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
-  return p.dt == FA_BF16 ? dq_typed<BF16>(p, t, stream) : dq_typed<F16>(p, t, stream);
+hipError_t launch_bwd_reduce(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
+  return p.dt == FA_BF16 ? reduce_typed<BF16>(p, t, stream) : reduce_typed<F16>(p, t, stream);
 }
 
 }  // namespace fa

@@ -6,10 +6,16 @@
 // rows may see (as in the forward, [BLOG] §五 outer loop over query tiles,
 // inner loop over key/value tiles) and per tile recompute
 //   S = scale Q K^T,  P = exp(S - LSE),  dP = dO V^T,  dS = P (dP - D),
-// with D_i = sum_c dO_ic O_ic from the first backward stage, then add
+// then add
 //   dQ += scale dS K.
 // dQ stays in registers for the whole key range and is written once, in the
 // input dtype: no atomics, no float32 accumulator in memory.
+//
+// This is the first backward stage: each lane also forms its row's
+// D_i = sum_c dO_ic O_ic from the O and dO values it loads (its half of the
+// row's dims, plus the other half-wave's), and stores the row terms -D_i and
+// -LSE_i / scale that the key-block stage (fa_bwd.hip) starts its
+// accumulators from.
 //
 // gfx950 mapping (as the forward kernel): one query row per lane; S^T = K Q^T
 // and dP^T = V dO^T on v_mfma_f32_32x32x16 with Q and dO held as B operands
@@ -34,20 +40,22 @@ struct DqArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dO;
+  const uint16_t* o;
   const float* lse;
-  const float* nd;  // -D per query row
+  float* nd;    // out: -D per query row (-D / r with dropout)
+  float* lneg;  // out: -LSE / scale per query row (-inf: row saw no key)
   uint16_t* dq;
   int B, Hq, Hkv, G, Nq, Nkv, n_qtiles;
-  float scale, scale_log2;
+  float scale, scale_log2, inv_scale, inv_r;
   DropParams drop;  // used only by the dropout instantiations
 };
 
 // NW waves of 32 query rows per workgroup (8 when the grid fills the GPU,
 // else 4), as in the forward.
 //
-// DROP: dropout with keep factor r; the first stage stored -D / r in nd, so
-// dS / r = P ((Z ? dP : 0) - D / r), and dQ carries r at the end. The keep
-// words are drawn as in the forward.
+// DROP: dropout with keep factor r; the row term is -D / r (also stored in
+// nd), so dS / r = P ((Z ? dP : 0) - D / r), and dQ carries r at the end.
+// The keep words are drawn as in the forward.
 template <typename T, int D, bool CAUSAL, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   constexpr int BR = 32 * NW;
@@ -104,21 +112,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
     dma_tile<D, NW, DT::K_STEP>(vd, vhead, kv_bytes, j * BC, wave, src);
   };
 
-  // Q and dO of this lane's row as B operands; its LSE (log2 units; +inf for
-  // a row that saw no key, so P = 0) and D.
-  const uint16_t* qp = a.q + (bh * Nq + qrow) * D;
-  const uint16_t* gp = a.dO + (bh * Nq + qrow) * D;
+  // Q and dO of this lane's row as B operands (dims 16 kc + 8 h .. + 7), its
+  // LSE (log2 units; +inf for a row that saw no key, so P = 0) and the row
+  // term -D, D summed over this lane's dims and then the other half-wave's.
+  const size_t row_off = bh * Nq + qrow;
+  const uint16_t* qp = a.q + row_off * D;
+  const uint16_t* gp = a.dO + row_off * D;
+  const uint16_t* op = a.o + row_off * D;
   V8 qf[KC], gf[KC];
+  float dsum = 0.0f;
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
+    const u32x4 g = has_row ? ld16(gp + kc * 16 + h * 8) : zero_u32x4();
+    const u32x4 ov = has_row ? ld16(op + kc * 16 + h * 8) : zero_u32x4();
     qf[kc] = as_vec8<T>(has_row ? ld16(qp + kc * 16 + h * 8) : zero_u32x4());
-    gf[kc] = as_vec8<T>(has_row ? ld16(gp + kc * 16 + h * 8) : zero_u32x4());
+    gf[kc] = as_vec8<T>(g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dsum = fmaf(T::to_float(ov[i] & 0xffffu), T::to_float(g[i] & 0xffffu), dsum);
+      dsum = fmaf(T::to_float(ov[i] >> 16), T::to_float(g[i] >> 16), dsum);
+    }
   }
-  float lse2 = INFINITY, ndrow = 0.0f;
+  const float ndrow = -(dsum + swap_halves(dsum)) * a.inv_r;
+  float lse2 = INFINITY;
   if (has_row) {
-    const float l = a.lse[bh * Nq + qrow];
+    const float l = a.lse[row_off];
     if (l != -INFINITY) lse2 = l * LOG2E;
-    ndrow = a.nd[bh * Nq + qrow];
+    if (h == 0) {
+      a.nd[row_off] = ndrow;
+      a.lneg[row_off] = l == -INFINITY ? -INFINITY : -l * a.inv_scale;
+    }
   }
   const float sl2 = a.scale_log2;
 
@@ -265,8 +288,10 @@ hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   a.k = static_cast<const uint16_t*>(t.k);
   a.v = static_cast<const uint16_t*>(t.v);
   a.dO = static_cast<const uint16_t*>(t.dO);
+  a.o = static_cast<const uint16_t*>(t.o);
   a.lse = t.lse;
   a.nd = t.nd;
+  a.lneg = t.lneg;
   a.dq = static_cast<uint16_t*>(t.dq);
   a.B = p.B;
   a.Hq = p.Hq;
@@ -277,6 +302,8 @@ hipError_t launch_nw(const Problem& p, const BwdPtrs& t, hipStream_t stream) {
   a.n_qtiles = (p.Nq + 32 * NW - 1) / (32 * NW);
   a.scale = p.scale;
   a.scale_log2 = p.scale * LOG2E;
+  a.inv_scale = 1.0f / p.scale;
+  a.inv_r = t.drop ? 1.0f / t.drop->rscale : 1.0f;
   a.drop = t.drop ? *t.drop : DropParams{0, 0, 0, 1.0f};
   dim3 grid((unsigned)(a.n_qtiles * p.B * p.Hq));
   if (p.causal)

@@ -91,10 +91,10 @@ hipError_t launch_decode_paged(const Problem& p, const FwdPtrs& t, const PagedPt
                                hipStream_t stream);
 hipError_t launch_dropout_mask(uint8_t* keep, int B, int Hq, int Nq, int Nkv, const DropParams& dp,
                                hipStream_t stream);
-hipError_t launch_bwd_pre(const Problem& p, const BwdPtrs& t, hipStream_t stream);
-hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);
-hipError_t launch_bwd_dq(const Problem& p, const BwdPtrs& t, hipStream_t stream);
-// The query-stationary dQ kernel (part of launch_bwd_dq).
+// Backward stages, in order: dQ and the row terms (fa_bwd_dq.hip); dK, dV
+// per key block; the sum of split dK, dV partials (no-op unless split).
 hipError_t launch_bwd_dq_rows(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+hipError_t launch_bwd_main(const Problem& p, const BwdPtrs& t, hipStream_t stream);
+hipError_t launch_bwd_reduce(const Problem& p, const BwdPtrs& t, hipStream_t stream);
 
 }  // namespace fa

@@ -111,12 +111,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
 /* One stage of fa_bwd, same arguments, for callers that interleave or time
  * the stages. Stages must run in order 0, 1, 2 on one workspace:
- *   0  the row terms -D_i and -LSE_i / scale into the workspace;
+ *   0  per query tile: recompute P and dS over the key/value tiles it sees
+ *      and write dq; store the row terms -D_i and -LSE_i / scale into the
+ *      workspace;
  *   1  per key/value block: recompute P and dS over the query tiles that see
- *      it and write dk, dv (float32 partials into the workspace when the
- *      query-head group is split);
- *   2  per query tile: recompute P and dS over the key/value tiles it sees
- *      and write dq; add up split dk, dv partials.
+ *      it (from stage 0's row terms) and write dk, dv (float32 partials into
+ *      the workspace when the query-head group is split);
+ *   2  add up split dk, dv partials (enqueues nothing when the group is not
+ *      split).
  * Any other stage value returns FA_ERR_UNSUPPORTED. */
 int fa_bwd_stage(int stage,
                  const void* q, const void* k, const void* v, const void* o, const float* lse,
