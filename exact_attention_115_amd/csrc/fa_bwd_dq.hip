@@ -115,34 +115,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   // Q and dO of this lane's row as B operands (dims 16 kc + 8 h .. + 7), its
   // LSE (log2 units; +inf for a row that saw no key, so P = 0) and the row
   // term -D, D summed over this lane's dims and then the other half-wave's.
-  const size_t row_off = bh * Nq + qrow;
+  // A lane past the last row loads row N_q - 1 instead: the loads then need
+  // no branch and issue back to back. Such a lane's results stay in its own
+  // registers (every value below is per row) and are never stored.
+  const size_t row_off = bh * Nq + min(qrow, Nq - 1);
   const uint16_t* qp = a.q + row_off * D;
   const uint16_t* gp = a.dO + row_off * D;
   const uint16_t* op = a.o + row_off * D;
+  const float lse_row = a.lse[row_off];
   V8 qf[KC], gf[KC];
-  float dsum = 0.0f;
+  u32x4 gb[KC], ob[KC];  // dO and O of the same dims, for D
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    const u32x4 g = has_row ? ld16(gp + kc * 16 + h * 8) : zero_u32x4();
-    const u32x4 ov = has_row ? ld16(op + kc * 16 + h * 8) : zero_u32x4();
-    qf[kc] = as_vec8<T>(has_row ? ld16(qp + kc * 16 + h * 8) : zero_u32x4());
-    gf[kc] = as_vec8<T>(g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dsum = fmaf(T::to_float(ov[i] & 0xffffu), T::to_float(g[i] & 0xffffu), dsum);
-      dsum = fmaf(T::to_float(ov[i] >> 16), T::to_float(g[i] >> 16), dsum);
-    }
+    gb[kc] = ld16(gp + kc * 16 + h * 8);
+    ob[kc] = ld16(op + kc * 16 + h * 8);
+    qf[kc] = as_vec8<T>(ld16(qp + kc * 16 + h * 8));
+    gf[kc] = as_vec8<T>(gb[kc]);
   }
-  const float ndrow = -(dsum + swap_halves(dsum)) * a.inv_r;
-  float lse2 = INFINITY;
-  if (has_row) {
-    const float l = a.lse[row_off];
-    if (l != -INFINITY) lse2 = l * LOG2E;
-    if (h == 0) {
-      a.nd[row_off] = ndrow;
-      a.lneg[row_off] = l == -INFINITY ? -INFINITY : -l * a.inv_scale;
-    }
-  }
+  __builtin_amdgcn_sched_barrier(0);  // all row loads issue before the first copy
+  // Set once the first K/V tile's copy is in flight (see below).
+  float lse2 = INFINITY, ndrow = 0.0f;
   const float sl2 = a.scale_log2;
 
   f32x16 acc[OD];
@@ -252,6 +244,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   // others (last read during tile j - 1; every wave passed the barrier that
   // ended it). Every wave runs n_tiles rounds and computes the first n_w.
   load_kv(0, kbuf0, vbuf0);
+  __builtin_amdgcn_sched_barrier(0);
+  // The row terms, while the first tile's copy is in flight.
+  {
+    float dsum = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dsum = fmaf(T::to_float(ob[kc][i] & 0xffffu), T::to_float(gb[kc][i] & 0xffffu), dsum);
+        dsum = fmaf(T::to_float(ob[kc][i] >> 16), T::to_float(gb[kc][i] >> 16), dsum);
+      }
+    ndrow = -(dsum + swap_halves(dsum)) * a.inv_r;
+    if (has_row) {
+      if (lse_row != -INFINITY) lse2 = lse_row * LOG2E;
+      if (h == 0) {
+        a.nd[row_off] = ndrow;
+        a.lneg[row_off] = lse_row == -INFINITY ? -INFINITY : -lse_row * a.inv_scale;
+      }
+    }
+  }
   __syncthreads();
   for (int j = 0; j < n_tiles; j += 2) {
     load_kv(j + 1, kbuf1, vbuf1);
