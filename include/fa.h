@@ -79,8 +79,9 @@ enum {
 size_t fa_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int d, fa_dtype dt);
 
 /* Bytes of device workspace fa_bwd needs: the float32 row terms -D_i
- * (D_i = sum_c dO_ic O_ic) and -LSE_i / scale, each [B, Hq, N_q], and, when
- * there are too few key blocks
+ * (D_i = sum_c dO_ic O_ic) and -LSE_i / scale, each [B, Hq, N_q] (at byte
+ * offsets 0 and R = 4 B Hq N_q rounded up to a multiple of 256; -D_i / r
+ * with dropout), and, when there are too few key blocks
  * to fill the GPU (e.g. MQA), float32 partial dK and dV sums of the split
  * query-head groups. Linear in N ([KB] §06: storage O(N), not O(N^2)).
  * Returns 0 for an invalid or empty problem. */

@@ -150,9 +150,36 @@ def test_stages_equal_fused_and_deterministic():
     for stage in range(3):
         assert fa.fa_bwd_stage(stage, qg, kg, vg, o, lse, dog, dq2, dk2, dv2, ws, w.scale, True) == 0
     torch.cuda.synchronize()
-    # dK, dV: no atomics, bitwise reproducible. dQ: atomics, order may vary.
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
-    assert ((dq1.float() - dq2.float()).abs().max() <= 1e-2).item()
+    # No atomics anywhere: all three gradients are bitwise reproducible.
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2) and torch.equal(dq1, dq2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stage0_row_terms(dtype):
+    """Stage 0 (the dQ kernel) leaves the row terms -D_i = -sum_c dO_ic O_ic
+    and -LSE_i / scale of every row in the workspace, at the offsets the
+    header states; ragged N_q, one kv head for three q heads."""
+    say(f"bwd stage-0 row terms {dtype}")
+    B, Hq, Hkv, N, d = 2, 3, 1, 300, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = random_tensors((B, Hq, N, d), (B, Hkv, N, d), dtype, seed=14, with_grad=True)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = fa.forward(qg, kg, vg, causal=True, scale=scale)
+    nbytes = fa.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, q.dtype)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN floats
+    dq, dk, dv = (torch.empty_like(t) for t in (qg, kg, vg))
+    assert fa.fa_bwd_stage(0, qg, kg, vg, o, lse, dog, dq, dk, dv, ws, scale, True) == 0
+    torch.cuda.synchronize()
+    rows = B * Hq * N
+    off = (rows * 4 + 255) // 256 * 256
+    nd = ws[:rows * 4].view(torch.float32).cpu().double().numpy()
+    lneg = ws[off:off + rows * 4].view(torch.float32).cpu().double().numpy()
+    prod = to_f64(o.cpu()).reshape(rows, d) * to_f64(do).reshape(rows, d)
+    D = prod.sum(axis=1)
+    # float32 sum of d products: |error| <= d * 2^-24 * sum |terms|.
+    assert np.all(np.abs(nd + D) <= d * 2.0**-24 * np.abs(prod).sum(axis=1) + 1e-30)
+    want = -to_f64(lse.cpu()).reshape(rows) / scale
+    assert np.all(np.abs(lneg - want) <= 2.0**-22 * np.abs(want))
 
 
 def test_empty_query_side_clears_key_gradients():
