@@ -355,7 +355,11 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
     a.part_lse[row * a.splits + split] = L > 0.0f ? (M + __log2f(L)) * LN2 : -INFINITY;
 }
 
-// Merge the splits of one (b, q head) row; one wave per row.
+// Merge the splits of one (b, q head) row with the [KB] §04 rescaling rule
+// (O = sum_s w_s O_s / sum_s w_s, w_s = exp(LSE_s - max LSE), LSE = max +
+// ln sum_s w_s); one wave per row. Lane s holds split s's LSE and weight
+// (64 splits per round); the partial outputs are read eight splits at a
+// time, all eight loads in flight together, in split order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_lse,
@@ -367,20 +371,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   if (row >= rows) return;
   const float* pl = part_lse + (size_t)row * splits;
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, pl[s]);
+  for (int s = lane; s < splits; s += 64) m = fmaxf(m, pl[s]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
   constexpr int PER = D / 64;
+  constexpr int U = 8;  // splits whose partial outputs are loaded together
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
   float sum = 0.0f;
   if (m != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float w = __expf(pl[s] - m);
-      sum += w;
-      const float* po = part_o + ((size_t)row * splits + s) * D;
+    const float* po = part_o + (size_t)row * splits * D + lane;
+    for (int s0 = 0; s0 < splits; s0 += 64) {
+      const int n = min(64, splits - s0);
+      const float w_lane = lane < n ? __expf(pl[s0 + lane] - m) : 0.0f;
+      sum += w_lane;
+      for (int j = 0; j < n; j += U) {
+        float x[U][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, po[lane + 64 * i], acc[i]);
+        for (int u = 0; u < U; ++u) {
+          const int s = s0 + min(j + u, n - 1);  // past the last split: reread it, weight 0
+#pragma unroll
+          for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)s * D + 64 * i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = __shfl(w_lane, j + u, 64);  // 0 for j + u >= n
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, x[u][i], acc[i]);
+        }
+      }
     }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) sum += __shfl_xor(sum, x, 64);
   }
   const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
 #pragma unroll
