@@ -357,9 +357,10 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
 
 // Merge the splits of one (b, q head) row with the [KB] §04 rescaling rule
 // (O = sum_s w_s O_s / sum_s w_s, w_s = exp(LSE_s - max LSE), LSE = max +
-// ln sum_s w_s); one wave per row. Lane s holds split s's LSE and weight
-// (64 splits per round); the partial outputs are read eight splits at a
-// time, all eight loads in flight together, in split order.
+// ln sum_s w_s); one wave per row. Lane l holds the LSE and weight of split
+// 64 r + l in round r; the partial outputs are read sixteen splits at a
+// time, the first sixteen while the LSEs are reduced, and added in split
+// order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_lse,
@@ -369,41 +370,48 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
-  const float* pl = part_lse + (size_t)row * splits;
-  float m = -INFINITY;
-  for (int s = lane; s < splits; s += 64) m = fmaxf(m, pl[s]);
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
   constexpr int PER = D / 64;
-  constexpr int U = 8;  // splits whose partial outputs are loaded together
+  constexpr int U = 16;  // splits whose partial outputs are loaded together
+  const float* pl = part_lse + (size_t)row * splits;
+  const float* po = part_o + (size_t)row * splits * D + lane;
+  float x[U][PER];
+  auto load_group = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, splits - 1);  // past the last split: reread it, weight 0
+#pragma unroll
+      for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)s * D + 64 * i];
+    }
+  };
+  const float l0 = lane < splits ? pl[lane] : -INFINITY;
+  load_group(0);
+  float m = l0;
+  for (int s = lane + 64; s < splits; s += 64) m = fmaxf(m, pl[s]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
   float sum = 0.0f;
   if (m != -INFINITY) {
-    const float* po = part_o + (size_t)row * splits * D + lane;
-    for (int s0 = 0; s0 < splits; s0 += 64) {
-      const int n = min(64, splits - s0);
-      const float w_lane = lane < n ? __expf(pl[s0 + lane] - m) : 0.0f;
-      sum += w_lane;
-      for (int j = 0; j < n; j += U) {
-        float x[U][PER];
+    float w_lane = 0.0f;
+    for (int s0 = 0; s0 < splits; s0 += U) {
+      if ((s0 & 63) == 0) {
+        const int s = s0 + lane;
+        const float l = s0 == 0 ? l0 : (s < splits ? pl[s] : -INFINITY);
+        w_lane = s < splits ? __expf(l - m) : 0.0f;
+        sum += w_lane;
+      }
+      if (s0 > 0) load_group(s0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int s = s0 + min(j + u, n - 1);  // past the last split: reread it, weight 0
+      for (int u = 0; u < U; ++u) {
+        const float w = __shfl(w_lane, (s0 & 63) + u, 64);  // 0 past the last split
 #pragma unroll
-          for (int i = 0; i < PER; ++i) x[u][i] = po[(size_t)s * D + 64 * i];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float w = __shfl(w_lane, j + u, 64);  // 0 for j + u >= n
-#pragma unroll
-          for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, x[u][i], acc[i]);
-        }
+        for (int i = 0; i < PER; ++i) acc[i] = fmaf(w, x[u][i], acc[i]);
       }
     }
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) sum += __shfl_xor(sum, x, 64);
+    for (int k = 32; k >= 1; k >>= 1) sum += __shfl_xor(sum, k, 64);
   }
   const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
 #pragma unroll
