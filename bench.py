@@ -347,8 +347,12 @@ def main():
     ms_per_step = ms_total / args.steps
     per_kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
                      for j, n in enumerate(names)}
-    if cold:
-        # Time per call between its own events (the flushes are not counted).
+    if w.Nq == 1:
+        # Decode: time per call between its own events. From cold caches the
+        # flushes are not counted; with warm caches a call (about 20 us at
+        # Hkv = 1) is shorter than the host's time to enqueue the next one,
+        # so the wall time between the first and last event would measure
+        # the host, not the GPU.
         ms_per_step = sum(per_kernel_ms.values())
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
