@@ -88,6 +88,11 @@ def parse():
                          "forward only")
     ap.add_argument("--warm-cache", action="store_true",
                     help="decode workloads: skip the cache flush before each timed call")
+    ap.add_argument("--inputs", choices=("randn", "const"), default="randn",
+                    help="development measurement only: 'const' sets every element of q, k, v, "
+                         "dO to 0.5 (the same instruction stream with operands that do not "
+                         "toggle, to see how much of the time is the clock the chip holds "
+                         "under power); the metric is defined on the default N(0,1) draws")
     return ap.parse_args()
 
 
@@ -225,6 +230,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     q, k, v, do = make_inputs(w)
+    if args.inputs == "const":
+        for t in (q, k, v, do):
+            if t is not None:
+                t.fill_(0.5)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
     do = do.to(dev) if do is not None else None
     o = torch.empty_like(q)
@@ -357,10 +366,12 @@ def main():
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if bwd else 0.0)
     out = {
-        "metric": (METRIC if args.workload == "c3" and not drop and not fp8
+        "metric": (METRIC if args.workload == "c3" and not drop and not fp8 and args.inputs == "randn"
                    else f"attention throughput, {args.workload}"
                    + (f" with dropout p={args.dropout}" if drop else "")
-                   + (" FP8 (E4M3) forward" if fp8 else "")),
+                   + (" FP8 (E4M3) forward" if fp8 else "")
+                   + (" on constant inputs (development measurement)"
+                      if args.inputs == "const" else "")),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -369,7 +380,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8 e4m3 (bf16 out)" if fp8 else w.dtype,
-        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to the storage dtype",
+        "data": ("synthetic: seeded i.i.d. N(0,1) q, k, v, dO rounded to the storage dtype"
+                 if args.inputs == "randn" else "synthetic: every element of q, k, v, dO = 0.5"),
         "config": {"workload": f"{'causal' if w.causal else 'non-causal'} attention "
                                f"{'forward+backward' if bwd else 'forward'} B={w.B} Hq={w.Hq} "
                                f"Hkv={w.Hkv} N_q={w.Nq} N_kv={w.Nkv} d={w.d} {w.dtype}"
