@@ -152,6 +152,7 @@ EDGE = [
     (1, 1, 1, 2, 4, 128, True),
     (3, 6, 3, 65, 129, 64, True),
     (1, 2, 1, 1, 1000, 128, True),     # decode, ragged split
+    (2, 4, 1, 1, 12763, 128, False),   # decode, 100 key-range splits: two merge rounds of 64, last group of 16 partial
     (2, 8, 2, 1, 64, 64, False),
     (2, 64, 16, 1000, 1000, 128, True),  # many 128-row workgroups, ragged last tile
     (4, 32, 32, 700, 900, 64, False),    # many workgroups, N_q < N_kv
