@@ -151,21 +151,45 @@ __device__ __forceinline__ void dkdv_step(
     const int y = t & 1, ch = (t >> 1) / OD, od = (t >> 1) % OD;
     return load_kt_dma<T, D>(y ? qp : gp, kt0, kt1, ch, od);
   };
-  init_rows(ln, h, sn);
-  init_rows(dn, h, dpn);
+  // With PREV the step opens with LEAD transposed products, which need no
+  // row terms: their operands are read first, then the row terms of tile
+  // i + 1 (16 reads) and the first row operands, so the first products do
+  // not wait for the row-term reads (LDS returns in order).
+  constexpr int LEAD = PREV ? 4 : 0;
   u32x4 rf[NR];
   V8 tf[NT];
-  rf[0] = rfrag(0);
-  rf[1] = rfrag(1);
   if constexpr (PREV) {
     tf[0] = tfrag(0);
     tf[1] = tfrag(1);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  init_rows(ln, h, sn);
+  init_rows(dn, h, dpn);
+  rf[0] = rfrag(0);
+  rf[1] = rfrag(1);
+  __builtin_amdgcn_sched_barrier(0);
   float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const int i = m >> 1;
-    if ((m & 1) == 0) {
+    // Product of slot m: without PREV, row product m / 2 on even slots;
+    // with PREV, transposed products 0 .. LEAD - 1, then row j and
+    // transposed j + LEAD alternating, then the last LEAD row products.
+    bool is_row;
+    int i;
+    if constexpr (!PREV) {
+      is_row = (m & 1) == 0;
+      i = m >> 1;
+    } else if (m < LEAD) {
+      is_row = false;
+      i = m;
+    } else if (m < LEAD + 2 * (NT - LEAD)) {
+      is_row = ((m - LEAD) & 1) == 0;
+      i = ((m - LEAD) >> 1) + (is_row ? 0 : LEAD);
+    } else {
+      is_row = true;
+      i = m - NT;
+    }
+    if (is_row) {
       if (i + 2 < NR) rf[i + 2] = rfrag(i + 2);
       const int x = i & 1, qb = (i >> 1) & 1, kc = i >> 2;
       if (x)
