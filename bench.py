@@ -20,9 +20,11 @@ query-tile kernel recomputes are an implementation cost and are not counted.
 
 Warm-up: the GPU reaches its steady clock only after some tens of
 milliseconds under load; at the default workload the first ~50 steps run up
-to ~15 % slower than the later ones. The default of 100 untimed warm-up
-steps (about 70 ms) therefore precedes the 50 timed ones; ``--warmup`` and
-``--steps`` override both.
+to ~15 % slower than the later ones. Before the ``--warmup`` untimed steps
+the bench therefore runs untimed steps for ``--settle-ms`` milliseconds of
+wall time (default 150; 0 turns it off), so that a short warm-up (say 5
+steps) does not leave the clock still rising inside the timed region. The
+settle time and the number of steps it ran are reported in the JSON line.
 
 Prints ONE JSON line. ``--workload`` selects another synthetic workload for
 development measurements (decode workloads report HBM GB/s, each timed call
@@ -74,6 +76,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed steps for this many ms of wall time before the warm-up, so "
+                         "the GPU clock has settled (0: none)")
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -329,6 +334,15 @@ def main():
                 if events is not None and s != 1:
                     events[2 + s // 2].record(stream)
 
+    settle_steps = 0
+    if args.settle_ms > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+            for _ in range(8):
+                step()
+            settle_steps += 8
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -375,6 +389,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "untimed_steps": settle_steps},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -115,6 +115,21 @@ def _dims(q: torch.Tensor, k: torch.Tensor):
     return B, Hq, Hkv, Nq, Nkv, d
 
 
+def _shape(name, t, shape):
+    """Raise ValueError unless tensor t (if given) has exactly this shape."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _fwd_shapes(q, k, v, o, lse):
+    """Shapes of a forward call: v like k, o like q, lse [B, Hq, N_q]."""
+    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
+    _shape("v", v, k.shape)
+    _shape("o", o, q.shape)
+    _shape("lse", lse, (B, Hq, Nq))
+    return B, Hq, Hkv, Nq, Nkv, d
+
+
 def _check(ts, dtype=None):
     for name, t in ts.items():
         if t is None:
@@ -139,10 +154,10 @@ def fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, dtype) -> int:
 
 def fa_fwd(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None) -> int:
     """Call fa_fwd on tensors; returns the status code (no exception)."""
+    B, Hq, Hkv, Nq, Nkv, d = _fwd_shapes(q, k, v, o, lse)
     _check({"q": q, "k": k, "v": v, "o": o}, q.dtype)
     _check({"lse": lse}, torch.float32)
     _check({"workspace": workspace})
-    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
                          B, Hq, Hkv, Nq, Nkv, d, float(scale), int(bool(causal)), _dtype_code(q),
@@ -150,10 +165,14 @@ def fa_fwd(q, k, v, o, lse, workspace, scale: float, causal: bool, stream=None) 
 
 
 def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream):
+    B, Hq, Hkv, Nq, Nkv, d = _fwd_shapes(q, k, v, o, lse)
+    _shape("do", do, q.shape)
+    _shape("dq", dq, q.shape)
+    _shape("dk", dk, k.shape)
+    _shape("dv", dv, k.shape)
     _check({"q": q, "k": k, "v": v, "o": o, "do": do, "dq": dq, "dk": dk, "dv": dv}, q.dtype)
     _check({"lse": lse}, torch.float32)
     _check({"workspace": workspace})
-    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(workspace), ws_bytes, B, Hq, Hkv, Nq, Nkv, d, float(scale), int(bool(causal)),
@@ -227,13 +246,17 @@ def _paged_dims(q, k_pages, page_table):
 def fa_fwd_paged(q, k_pages, v_pages, page_table, seq_lens, o, lse, workspace, scale: float,
                  stream=None) -> int:
     """Call fa_fwd_paged on tensors; returns the status code (no exception)."""
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must have the same shape")
+    B, Hq, Hkv, num_pages, page_size, max_pages, d = _paged_dims(q, k_pages, page_table)
+    _shape("seq_lens", seq_lens, (B,))
+    _shape("o", o, q.shape)
+    if lse is not None and lse.numel() != B * Hq:
+        raise ValueError(f"lse has {lse.numel()} elements, expected B * Hq = {B * Hq}")
     _check({"q": q, "k_pages": k_pages, "v_pages": v_pages, "o": o}, q.dtype)
     _check({"page_table": page_table, "seq_lens": seq_lens}, torch.int32)
     _check({"lse": lse}, torch.float32)
     _check({"workspace": workspace})
-    if v_pages.shape != k_pages.shape:
-        raise ValueError("k_pages and v_pages must have the same shape")
-    B, Hq, Hkv, num_pages, page_size, max_pages, d = _paged_dims(q, k_pages, page_table)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return load().fa_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
                                _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, B, Hq,
@@ -262,10 +285,10 @@ def forward_paged(q, k_pages, v_pages, page_table, seq_lens, scale: float | None
 def fa_fwd_dropout(q, k, v, o, lse, workspace, scale: float, causal: bool, dropout_p: float,
                    seed: int, offset: int = 0, stream=None) -> int:
     """Call fa_fwd_dropout on tensors; returns the status code (no exception)."""
+    B, Hq, Hkv, Nq, Nkv, d = _fwd_shapes(q, k, v, o, lse)
     _check({"q": q, "k": k, "v": v, "o": o}, q.dtype)
     _check({"lse": lse}, torch.float32)
     _check({"workspace": workspace})
-    B, Hq, Hkv, Nq, Nkv, d = _dims(q, k)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return load().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                  ws_bytes, B, Hq, Hkv, Nq, Nkv, d, float(scale),
@@ -337,13 +360,13 @@ def fa_fwd_fp8(q8, k8, v8, o, lse, scale: float, causal: bool, descale_q: float 
                descale_k: float = 1.0, descale_v: float = 1.0, stream=None) -> int:
     """Call fa_fwd_fp8 (E4M3 codes as uint8 or float8_e4m3fn tensors, o bf16);
     returns the status code (no exception)."""
+    B, Hq, Hkv, Nq, Nkv, d = _fwd_shapes(q8, k8, v8, o, lse)
     for name, t in {"q8": q8, "k8": k8, "v8": v8}.items():
         _check({name: t})
         if t.dtype not in _FP8_TYPES:
             raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), not {t.dtype}")
     _check({"o": o}, torch.bfloat16)
     _check({"lse": lse}, torch.float32)
-    B, Hq, Hkv, Nq, Nkv, d = _dims(q8, k8)
     return load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
                              Nkv, d, float(scale), int(bool(causal)), float(descale_q),
                              float(descale_k), float(descale_v), _stream(stream))

@@ -394,22 +394,24 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t kr1 = k_read_base<D>(h, c, 1);
   const uint32_t kt0 = kt_read_base<D>(h, c, 0);
   const uint32_t kt1 = kt_read_base<D>(h, c, 1);
-  const uint32_t q_bytes = (uint32_t)Nq * D * 2u;
-  const uint32_t row_bytes = (uint32_t)Nq * 4u;
   // Tile t (query head, first row) into slot x: Q and dO rows (reads past
   // N_q fill zeros, which add nothing to dK, dV), -LSE / scale and -D rows.
+  // Each copy's buffer resource starts at the tile's own first row (64-bit
+  // address arithmetic) and spans only the tile's rows, so the 32-bit range
+  // of the resource never depends on the length of the query sequence.
   auto load_tile = [&](int t, int x) __attribute__((always_inline)) {
     if (t >= total) return;
     const int hq = hq0 + t / per_head;
-    const int qi0 = (qt_begin + t % per_head) * BQ;
-    const size_t rb = (size_t)b * a.Hq + hq;
-    dma_tile<D, 4, DT::K_STEP>(qslot(x), a.q + rb * Nq * D, q_bytes, qi0, wave, src);
-    dma_tile<D, 4, DT::K_STEP>(gslot(x), a.dO + rb * Nq * D, q_bytes, qi0, wave, src);
+    const int qi0 = (qt_begin + t % per_head) * BQ;  // < Nq
+    const size_t r0 = ((size_t)b * a.Hq + hq) * Nq + qi0;
+    const uint32_t rows_left = (uint32_t)min(Nq - qi0, BQ);
+    const uint32_t tile_bytes = rows_left * (uint32_t)DT::RB;
+    dma_tile<D, 4, DT::K_STEP>(qslot(x), a.q + r0 * D, tile_bytes, 0, wave, src);
+    dma_tile<D, 4, DT::K_STEP>(gslot(x), a.dO + r0 * D, tile_bytes, 0, wave, src);
     if (wave < 2) {
-      const float* rows = (wave == 0 ? a.lneg : a.nd) + rb * Nq + qi0;
-      const uint32_t left = row_bytes - __builtin_amdgcn_readfirstlane(min(row_bytes, (uint32_t)qi0 * 4u));
+      const float* rows = (wave == 0 ? a.lneg : a.nd) + r0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          make_rsrc(rows, left),
+          make_rsrc(rows, rows_left * 4u),
           (__attribute__((address_space(3))) void*)(wave == 0 ? lslot(x) : dslot(x)), 4,
           (uint32_t)lane * 4u, 0, 0, 0);
     }

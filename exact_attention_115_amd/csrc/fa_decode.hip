@@ -33,7 +33,7 @@ struct DecArgs {
   float* part_o;    // [B*Hq][splits][D]
   float* part_lse;  // [B*Hq][splits]
   int Hq, Hkv, G, Nkv, splits, keys_per_split, n_qgroups;
-  uint32_t q_bytes;  // bytes of Q
+  int q_rows;        // rows of Q (B * Hq)
   float scale_log2;
   // Paged K/V: page_table [B, max_pages] (physical page of each logical
   // page), seq_lens [B]; Nkv = max_pages * page_size.
@@ -173,13 +173,24 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
   // Where tile j of the split comes from: a base pointer, the bytes that may
   // be read from it (reads past them fill zeros) and the tile's first key
   // relative to the base. Contiguous: the split's range. Paged: the tile's
-  // page (a page holds a whole number of 64-key tiles); a table entry out of
-  // [0, num_pages) reads as a page of zeros.
+  // page (a page holds a whole number of 64-key tiles); the table is read
+  // only for tiles before the sequence's end, and a tile whose entry is out
+  // of [0, num_pages) is not read at all (its keys are masked out below).
   struct Src {
     const uint16_t* k;
     const uint16_t* v;
     uint32_t bytes;
     int key0;
+  };
+  // Paged: the pool page of tile j, or -1 when the tile lies past the
+  // sequence's end or its table entry is out of range (uniform scalar).
+  auto tile_page = [&](int j) __attribute__((always_inline)) -> int {
+    const int key0 = key_begin + j * BC;  // key of the sequence
+    if (key0 >= key_end) return -1;
+    const int pg = __builtin_amdgcn_readfirstlane(key0 / a.page_size);  // < max_pages
+    const auto* table = (const __attribute__((address_space(4))) int*)a.page_table;
+    const int phys = table[(size_t)b * a.max_pages + pg];
+    return (phys >= 0 && phys < a.num_pages) ? phys : -1;
   };
   auto tile_src = [&](int j) __attribute__((always_inline)) -> Src {
     Src r;
@@ -191,10 +202,8 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
       r.key0 = j * BC;
     } else {
       const int key0 = key_begin + j * BC;  // key of the sequence
-      const int pg = __builtin_amdgcn_readfirstlane(min(key0 / a.page_size, a.max_pages - 1));
-      const auto* table = (const __attribute__((address_space(4))) int*)a.page_table;
-      const int phys = table[(size_t)b * a.max_pages + pg];
-      const bool ok = phys >= 0 && phys < a.num_pages && key0 < key_end;
+      const int phys = tile_page(j);
+      const bool ok = phys >= 0;
       const size_t off = (((size_t)(ok ? phys : 0) * a.Hkv + hkv) * a.page_size + key0 % a.page_size) * D;
       r.k = a.k + off;
       r.v = a.v + off;
@@ -222,8 +231,12 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
 
   // The group's Q rows (rows past the group's heads are loaded but unused),
   // copied by all waves; then each wave's first tile.
+  // The copy's buffer resource starts at the group's first row (64-bit
+  // address arithmetic) and spans at most its 32 rows, so its 32-bit range
+  // never depends on B * Hq.
   const size_t q_row0 = (size_t)b * a.Hq + hkv * a.G + qg * 32;
-  copy_blocks_async(qbuf, a.q, a.q_bytes, (uint32_t)(q_row0 * D * 2), wave, lane, QBLK);
+  const uint32_t q_left = (uint32_t)min((size_t)32, (size_t)a.q_rows - q_row0) * DT::RB;
+  copy_blocks_async(qbuf, a.q + q_row0 * D, q_left, 0u, wave, lane, QBLK);
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
   load_k(wave);
   load_v(wave);
@@ -262,12 +275,15 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
     // the split fill zeros, so every pass issues the same copies).
     wait_copies<CPT>();
     load_k(j + 4);
-    if (key0 + BC > key_end) {
+    // Keys past the end and, paged, every key of a tile whose table entry
+    // is out of range: such keys are dropped, not read as zeros.
+    const int key_lim = (PAGED && tile_page(j) < 0) ? key0 : key_end;
+    if (key0 + BC > key_lim) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key0 + kb * 32 + acc_key(h, r) >= key_end) s[kb][r] = -INFINITY;
+          if (key0 + kb * 32 + acc_key(h, r) >= key_lim) s[kb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -440,7 +456,7 @@ hipError_t launch_typed(const Problem& p, const FwdPtrs& t, const PagedPtrs* pg,
   a.splits = sp.splits;
   a.keys_per_split = sp.keys_per_split;
   a.n_qgroups = (p.G + 31) / 32;
-  a.q_bytes = (uint32_t)((size_t)p.B * p.Hq * D * 2);
+  a.q_rows = p.B * p.Hq;
   a.scale_log2 = p.scale * LOG2E;
   a.page_table = PAGED ? pg->page_table : nullptr;
   a.seq_lens = PAGED ? pg->seq_lens : nullptr;

@@ -33,6 +33,8 @@
  *   to nearest even.
  * Head dim d: 64 or 128. Sizes: N_kv * d < 2^29 (one head's K or V under
  *   2 GiB) and B * H * N < 2^31; larger problems return FA_ERR_UNSUPPORTED.
+ *   The query side (q, o, dO, dq, lse) is addressed with 64-bit offsets, so
+ *   one head's Q may exceed 4 GiB.
  * Pointers: device pointers, 16-byte aligned; the workspace 256-byte aligned.
  *   Outputs must not overlap inputs. Every output element is overwritten.
  * Ownership: the caller allocates and frees every buffer, including the
@@ -142,10 +144,11 @@ int fa_bwd_stage(int stage,
  *              sees all of them; causal masking has no effect with one row)
  *   o          [B, Hq, 1, d], dtype dt;  lse [B, Hq] float32
  * page_size must be a positive multiple of 64. Values in device memory are
- * not checked on the host: a table entry outside [0, num_pages) reads as a
- * page of zeros, and lengths are clamped to [0, max_pages * page_size]; a
- * sequence of length 0 gets o = 0, lse = -inf. Entries past a sequence's
- * pages are not read. The workspace (fa_fwd_paged_workspace_size) holds the
+ * not checked on the host: a table entry outside [0, num_pages) names no
+ * page, and the keys it would hold are dropped from the attention (never
+ * read, never scored); lengths are clamped to [0, max_pages * page_size]. A
+ * sequence of length 0, or whose every entry is out of range, gets o = 0,
+ * lse = -inf. Entries past a sequence's last page are not read. The workspace (fa_fwd_paged_workspace_size) holds the
  * float32 partial results of the key-range splits; 256-byte aligned. Same
  * status codes and aliasing rules as fa_fwd; asynchronous on stream. */
 int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -37,6 +37,9 @@ of each sequence gathered through its page-table row, then the definition.
 ``fp8``        the forward of E4M3 (8-bit float) inputs with per-tensor
                descale factors: their decoded values, then the definition;
                and the bound on what rounding P to E4M3 may change in O.
+``bounds``     magnitude sums of the gradients' terms, which bound what
+               rounding probabilities and dS to 16 bits may change in them
+               (used by the parity tests' element-wise gradient check).
 ``dropout``    dropout on the probabilities with a mask drawn from the
                counter-based generator Philox4x64-10 (readings in its
                docstring), forward and backward.
@@ -66,5 +69,10 @@ from .dropout import (  # noqa: F401
     threshold,
 )
 from .fp8 import decode as fp8_decode, head_forward_fp8, p_rounding_bound  # noqa: F401
+from .bounds import (  # noqa: F401
+    attention_backward_magnitudes,
+    group_backward_magnitudes,
+    head_backward_magnitudes,
+)
 from .online import online_row, online_forward  # noqa: F401
 from .brute import brute_forward  # noqa: F401

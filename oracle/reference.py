@@ -170,13 +170,20 @@ def paged_gather(pool, page_table_row, n_keys: int):
     """The first n_keys keys of one sequence from a page pool
     [num_pages, Hkv, page_size, d] and its row of the page table: logical page
     p (keys p*page_size ..) lives in pool page page_table_row[p]. Returns
-    [Hkv, n_keys, d]."""
-    page_size = pool.shape[2]
+    ([Hkv, n, d], valid [n]): keys whose table entry lies outside
+    [0, num_pages) name no page; they are returned as zeros and marked
+    invalid (reading: such keys are dropped from the attention)."""
+    num_pages, Hkv, page_size, d = pool.shape
     n_pages = -(-n_keys // page_size)
-    pages = [pool[int(page_table_row[p])] for p in range(n_pages)]
-    if not pages:
-        return np.zeros((pool.shape[1], 0, pool.shape[3]))
-    return np.concatenate(pages, axis=1)[:, :n_keys]
+    if n_pages == 0:
+        return np.zeros((Hkv, 0, d)), np.zeros(0, dtype=bool)
+    pages, valid = [], []
+    for p in range(n_pages):
+        e = int(page_table_row[p])
+        ok = 0 <= e < num_pages
+        pages.append(pool[e] if ok else np.zeros((Hkv, page_size, d)))
+        valid.append(np.full(page_size, ok))
+    return np.concatenate(pages, axis=1)[:, :n_keys], np.concatenate(valid)[:n_keys]
 
 
 def paged_decode_forward(q, k_pages, v_pages, page_table, seq_lens, scale: float):
@@ -184,7 +191,8 @@ def paged_decode_forward(q, k_pages, v_pages, page_table, seq_lens, scale: float
     q [B, Hq, 1, d]; k_pages, v_pages [num_pages, Hkv, page_size, d];
     page_table [B, max_pages]; seq_lens [B]. Each sequence's K and V are
     gathered through its table row and the single query row attends to all of
-    them (no mask). Returns (O [B, Hq, 1, d], LSE [B, Hq, 1])."""
+    them (no mask), except keys whose table entry is out of range, which are
+    dropped. Returns (O [B, Hq, 1, d], LSE [B, Hq, 1])."""
     B, Hq = q.shape[0], q.shape[1]
     Hkv = k_pages.shape[1]
     G = Hq // Hkv
@@ -194,8 +202,11 @@ def paged_decode_forward(q, k_pages, v_pages, page_table, seq_lens, scale: float
         n = int(seq_lens[b])
         if n == 0:
             continue
-        kb = paged_gather(k_pages, page_table[b], n)
-        vb = paged_gather(v_pages, page_table[b], n)
+        kb, valid = paged_gather(k_pages, page_table[b], n)
+        vb, _ = paged_gather(v_pages, page_table[b], n)
+        kb, vb = kb[:, valid], vb[:, valid]
+        if kb.shape[1] == 0:
+            continue
         for h in range(Hq):
             o[b, h], lse[b, h] = head_forward(q[b, h], kb[h // G], vb[h // G], False, scale)
     return o, lse

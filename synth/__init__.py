@@ -144,3 +144,12 @@ def ramp_tensors(shape_q, shape_kv, dtype: str, seed: int, ramp: str, peak: floa
         raise ValueError(ramp)
     k = k * r[:, None]
     return q.to(dt), k.to(dt), v.to(dt), (do.to(dt) if do is not None else None)
+
+
+def random_device_tensor(shape, dtype: str, seed: int, device="cuda"):
+    """One i.i.d. N(0, 1) tensor drawn directly on the device (for inputs of
+    several GiB that are never drawn on the host): a device generator seeded
+    with ``seed`` draws the values in the storage dtype. Tests copy back the
+    rows the oracle needs, so both sides still see the same values."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=_DTYPES[dtype], device=device)

@@ -334,6 +334,33 @@ def test_paged_decode_equals_contiguous_decode(page_size):
         np.testing.assert_allclose(lse[b], lb[0], rtol=0, atol=1e-12)
 
 
+def test_paged_decode_out_of_range_entry_drops_its_keys():
+    """A table entry outside [0, num_pages) names no page: the oracle's
+    result is the definition over the sequence's keys with that page's keys
+    removed (sliced out of the contiguous arrays directly)."""
+    rng = np.random.default_rng(9)
+    ps, max_pages, d = 64, 4, 32
+    n = max_pages * ps
+    k = rng.standard_normal((1, 2, n, d))
+    v = rng.standard_normal((1, 2, n, d))
+    q = rng.standard_normal((1, 4, 1, d))
+    table = np.array([[2, 0, 3, 1]])
+    k_pages = np.stack([k[0, :, table[0].tolist().index(p) * ps:][:, :ps] for p in range(4)])
+    v_pages = np.stack([v[0, :, table[0].tolist().index(p) * ps:][:, :ps] for p in range(4)])
+    for bad_entry in (7, -1):
+        bad = table.copy()
+        bad[0, 1] = bad_entry
+        lens = np.array([3 * ps + 10])
+        o, lse = oracle.paged_decode_forward(q, k_pages, v_pages, bad, lens, 0.2)
+        keep = np.r_[0:ps, 2 * ps:3 * ps + 10]
+        o_ref, l_ref = oracle.attention_forward(q, k[:, :, keep], v[:, :, keep], False, 0.2)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
+    bad = np.array([[9, 9, 9, 9]])
+    o, lse = oracle.paged_decode_forward(q, k_pages, v_pages, bad, np.array([n]), 0.2)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
 def test_paged_decode_empty_sequence():
     """A sequence with no keys: O = 0, LSE = -inf (the no-key convention)."""
     rng = np.random.default_rng(8)
@@ -530,3 +557,86 @@ def test_fp8_p_rounding_bound_holds_for_rounded_p(causal):
     bound = f8.p_rounding_bound(q8, k8, v8, causal, scale, dq, dk, dv)
     assert np.all(np.abs(o_rounded - o_exact) <= bound + 1e-12)
     assert np.max(np.abs(o_rounded - o_exact)) > 0  # the rounding is visible
+
+
+# ------------------------------------------------- gradient error magnitudes
+
+from oracle import bounds as gb  # noqa: E402
+
+
+def test_gradient_magnitudes_hand_example_closed_form():
+    """dO = 1 on the worked example of [KB] §04: P = [.1, .2, .4, .3],
+    dP_j = V_j, O = D = 29 = Dabs, so A_j = P_j (V_j + 29) = [3.9, 9.8, 23.6,
+    20.7]; Mk_j = A_j |q|, Mq = sum_j A_j |k_j|, Mv_j = P_j."""
+    g, q, k, v = hand_example_inputs()
+    mq, mk, mv, cq, ck, cv, rq, rk, rv, lq = gb.head_backward_magnitudes(q, k, v, np.ones((1, 1)),
+                                                                         False, 1.0)
+    a = np.array([3.9, 9.8, 23.6, 20.7])
+    np.testing.assert_allclose(mk[:, 0], a, atol=1e-12)
+    assert mq[0, 0] == pytest.approx(9.8 * math.log(2) + 23.6 * math.log(4) + 20.7 * math.log(3), abs=1e-12)
+    np.testing.assert_allclose(mv[:, 0], g["full_weights"], atol=1e-12)
+    w = np.array([10.0, 20.0, 30.0, 40.0]) + 29 + 1     # |dP_j| + Dabs + 1
+    assert cq[0, 0] == pytest.approx(float(np.sum(w * np.abs(np.log(g["exp_scores"])))), abs=1e-12)
+    np.testing.assert_allclose(ck[:, 0], w, atol=1e-12)
+    np.testing.assert_allclose(cv[:, 0], 1.0)
+    # One term per dK / dV element: root-sum-square = magnitude sum.
+    np.testing.assert_allclose(rk, mk, atol=1e-12)
+    np.testing.assert_allclose(rv, mv, atol=1e-12)
+    rq_want = math.sqrt(sum((aj * math.log(ej)) ** 2 for aj, ej in zip(a, g["exp_scores"])))
+    assert rq[0, 0] == pytest.approx(rq_want, abs=1e-12)
+    # Common-mode D term of dQ: Dabs * sum_j P_j |k_j| = 29 * (.2 ln2 + .4 ln4 + .3 ln3).
+    assert lq[0, 0] == pytest.approx(29 * (0.2 * math.log(2) + 0.4 * math.log(4) + 0.3 * math.log(3)),
+                                     abs=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_magnitudes_dominate_gradients(causal):
+    """Triangle inequality: |dV| <= Mv, |dK| <= Mk, |dQ| <= Mq element by
+    element; with dO >= 0 the dV sum has no cancellation and Mv == dV."""
+    q, k, v, do = rnd((13, 6), 60), rnd((17, 6), 61), rnd((17, 6), 62), rnd((13, 6), 63)
+    dq, dk, dv = oracle.head_backward(q, k, v, do, causal, 0.6)
+    mq, mk, mv, _, _, _, rq, rk, rv, _ = gb.head_backward_magnitudes(q, k, v, do, causal, 0.6)
+    # sqrt(sum x^2) <= sum |x| <= sqrt(n) sqrt(sum x^2)
+    for m, rr, n in ((mq, rq, 17), (mk, rk, 13), (mv, rv, 13)):
+        assert np.all(rr <= m + 1e-12) and np.all(m <= np.sqrt(n) * rr + 1e-12)
+    assert np.all(np.abs(dq) <= mq + 1e-12)
+    assert np.all(np.abs(dk) <= mk + 1e-12)
+    assert np.all(np.abs(dv) <= mv + 1e-12)
+    _, _, dv_pos = oracle.head_backward(q, k, v, np.abs(do), causal, 0.6)
+    mv_pos = gb.head_backward_magnitudes(q, k, v, np.abs(do), causal, 0.6)[2]
+    np.testing.assert_allclose(mv_pos, dv_pos, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("dtype,u", [(torch.bfloat16, 2.0 ** -8), (torch.float16, 2.0 ** -11)])
+def test_gradient_bound_holds_for_rounded_p_and_ds(dtype, u):
+    """A backward that rounds P (for dV), dS (for dK, dQ) and the output O
+    (for D) to a 16-bit format with an independent rounder (torch) stays
+    within u Mv, 2u Mk, 2u Mq of the exact gradients (+ the subnormal term for
+    fp16), and the bound is not vacuous."""
+    rng = np.random.default_rng(64)
+    nq, nkv, d, scale = 48, 80, 16, 0.25
+    q, k, v, do = (rng.standard_normal(s) for s in [(nq, d), (nkv, d), (nkv, d), (nq, d)])
+    rd = lambda x: torch.from_numpy(x).to(dtype).to(torch.float64).numpy()  # noqa: E731
+    s = np.where(oracle.visible_mask(np.arange(nq), nq, nkv, True), scale * (q @ k.T), -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o16 = rd(p @ v)
+    dp = do @ v.T
+    ds16 = rd(p * (dp - np.sum(do * o16, axis=1, keepdims=True)))
+    got = (scale * (ds16 @ k), scale * (ds16.T @ q), rd(p).T @ do)
+    ref = oracle.head_backward(q, k, v, do, True, scale)
+    mq, mk, mv, cq, ck, cv, rq, rk, rv, lq = gb.head_backward_magnitudes(q, k, v, do, True, scale)
+    sub = 2.0 ** -25 if dtype == torch.float16 else 0.0
+    worst = 0.0
+    rows = lambda x: np.linalg.norm(x, axis=1)  # noqa: E731
+    for g, r, m, c, rr, lin, f in zip(got, ref, (mq, mk, mv), (cq, ck, cv), (rq, rk, rv),
+                                      (lq, 0 * mk, 0 * mv), (2, 2, 1)):
+        bound = f * u * m + sub * c
+        assert np.all(np.abs(g - r) <= bound + 1e-15)
+        worst = max(worst, float(np.max(np.abs(g - r) / (bound + 1e-300))))
+        # Rows: independent roundings add up like a random walk (about
+        # u R / sqrt(3) per element); 6 u R bounds them with room to spare.
+        allow = 6 * u * rows(rr) + u * rows(lin) + sub * rows(c + 1)
+        assert np.all(rows(g - r) <= allow + 1e-15)
+        assert np.max(rows(g - r) / (allow + 1e-300)) < 0.5
+    assert worst > 0.01

@@ -13,7 +13,8 @@ import torch
 import exact_attention_115_amd as fa
 import oracle
 from synth import WORKLOADS, make_inputs, random_tensors, to_f64
-from tests.parity_util import check_grads, gpu, oracle_heads_backward, say
+from tests.parity_util import (all_finite, backward_nan_filled, check_grads, forward_nan_filled,
+                               full_magnitudes, gpu, oracle_heads_backward, say)
 
 pytestmark = [
     pytest.mark.gpu,
@@ -39,26 +40,45 @@ def test_c2_backward(name):
     say(f"{name}: {w}")
     q, k, v, do = make_inputs(w)
     _, grads = run_fwd_bwd(q, k, v, do, w.causal, w.scale)
-    check_grads(grads, full_oracle_bwd(q, k, v, do, w.causal, w.scale), w.dtype, name)
+    check_grads(grads, full_oracle_bwd(q, k, v, do, w.causal, w.scale), w.dtype, name,
+                mags=full_magnitudes(q, k, v, do, w.causal, w.scale))
+
+
+# kv heads compared with the oracle at full size. The grids keep all
+# workgroups of kv head h on XCD h mod 8; at c3 the four heads lie on four
+# different XCDs and include both ends of the head range.
+FULL_KV_HEADS = {
+    "c3": [(0, 0), (0, 9), (0, 22), (0, 31)],
+    "c4": [(0, 0), (0, 31)],
+    "c5g": [(0, 0), (3, 7)],
+    "c5m": [(2, 0)],
+}
 
 
 @pytest.mark.parametrize("name", ["c3", "c4", "c5g", "c5m"])
 def test_full_size_backward_sampled_heads(name):
-    """Full-size launch; the oracle computes complete kv-head groups (every q
-    head that reads a sampled kv head), which is all dK / dV depend on."""
+    """Full-size launch (the bench's launch configuration) into NaN-filled
+    gradient buffers and workspace: every element must be written and finite.
+    The oracle computes complete kv-head groups (every q head that reads a
+    sampled kv head), which is all dK / dV of that head depend on; each is
+    compared element by element."""
     w = WORKLOADS[name]
     say(f"{name}: {w}")
     q, k, v, do = make_inputs(w)
-    _, (dq, dk, dv) = run_fwd_bwd(q, k, v, do, w.causal, w.scale)
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = forward_nan_filled(qg, kg, vg, w.causal, w.scale)
+    dq, dk, dv = backward_nan_filled(qg, kg, vg, o, lse, dog, w.causal, w.scale)
+    torch.cuda.synchronize()
+    for nm, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        all_finite(f"{name} {nm}", t)
     G = w.Hq // w.Hkv
-    n = 1 if (w.Nq >= 8192 or G >= 32) else 2
-    heads_kv = [(0, 0), (w.B - 1, w.Hkv - 1)][:n]
-    refs = oracle_heads_backward(q, k, v, do, w.causal, w.scale, heads_kv)
-    for (b, hk), (dq_r, dk_r, dv_r) in zip(heads_kv, refs):
+    heads_kv = FULL_KV_HEADS[name]
+    refs = oracle_heads_backward(q, k, v, do, w.causal, w.scale, heads_kv, with_mags=True)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for (b, hk), (dq_r, dk_r, dv_r, mags) in zip(heads_kv, refs):
         dq_g = dq[b, hk * G:(hk + 1) * G]
-        check_grads((dq_g, dk[b, hk], dv[b, hk]), (dq_r, dk_r, dv_r), w.dtype, f"{name} kv head {(b, hk)}")
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
+        check_grads((dq_g, dk[b, hk], dv[b, hk]), (dq_r, dk_r, dv_r), w.dtype,
+                    f"{name} kv head {(b, hk)}", mags=mags)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -69,14 +89,18 @@ def test_long_ragged_backward_sampled_heads(causal):
                                 causal=causal, seed=38)
     say(f"{w}")
     q, k, v, do = make_inputs(w)
-    _, (dq, dk, dv) = run_fwd_bwd(q, k, v, do, w.causal, w.scale)
-    heads_kv = [(0, w.Hkv - 1)]
-    refs = oracle_heads_backward(q, k, v, do, w.causal, w.scale, heads_kv)
-    for (b, hk), (dq_r, dk_r, dv_r) in zip(heads_kv, refs):
+    qg, kg, vg, dog = gpu(q), gpu(k), gpu(v), gpu(do)
+    o, lse = forward_nan_filled(qg, kg, vg, w.causal, w.scale)
+    dq, dk, dv = backward_nan_filled(qg, kg, vg, o, lse, dog, w.causal, w.scale)
+    torch.cuda.synchronize()
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        all_finite(f"long ragged {nm}", t)
+    heads_kv = [(0, 0), (0, w.Hkv - 1)]
+    refs = oracle_heads_backward(q, k, v, do, w.causal, w.scale, heads_kv, with_mags=True)
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for (b, hk), (dq_r, dk_r, dv_r, mags) in zip(heads_kv, refs):
         check_grads((dq[b, hk:hk + 1], dk[b, hk], dv[b, hk]), (dq_r, dk_r, dv_r), w.dtype,
-                    f"long ragged causal={causal}")
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
+                    f"long ragged causal={causal} kv head {hk}", mags=mags)
 
 
 EDGE = [
@@ -103,7 +127,7 @@ def test_backward_edge_cases(dtype, case):
     scale = 1.0 / math.sqrt(d)
     _, grads = run_fwd_bwd(q, k, v, do, causal, scale)
     ref = full_oracle_bwd(q, k, v, do, causal, scale)
-    check_grads(grads, ref, dtype, str(case))
+    check_grads(grads, ref, dtype, str(case), mags=full_magnitudes(q, k, v, do, causal, scale))
 
 
 def test_rows_without_keys_pass_no_gradient():

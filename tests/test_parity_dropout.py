@@ -14,8 +14,9 @@ import pytest
 import torch
 
 import exact_attention_115_amd as fa
+import oracle
 from oracle import dropout as drop
-from parity_util import TOL, gpu, say
+from parity_util import TOL, check_grads, gpu, say
 from synth import WORKLOADS, make_inputs, random_tensors, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -129,15 +130,18 @@ def test_forward_dropout_repeatable_and_mask_dependent():
 # ------------------------------------------------------------------ backward
 
 def check_dropout_grads(grads, q, k, v, do, causal, scale, p, seed, offset, dtype, label):
-    g_ref = drop.attention_backward_dropout(to_f64(q), to_f64(k), to_f64(v), to_f64(do), causal,
-                                            scale, f32(p), seed, offset)
-    tol = TOL[dtype]["grad_rel"]
-    for name, g, r in zip(("dq", "dk", "dv"), grads, g_ref):
-        gg = to_f64(g)
-        assert np.all(np.isfinite(gg)), name
-        rel = float(np.linalg.norm(gg - r) / max(np.linalg.norm(r), 1e-30))
-        say(f"  [{label}] {name} Frobenius rel {rel:.3e}")
-        assert rel <= tol, (name, rel)
+    """Gradients against the dropout oracle, with the element-wise checks of
+    parity_util.check_grads and its rounding bound on the magnitudes of the
+    dropout backward's terms (the same keep masks)."""
+    q64, k64, v64, do64 = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    g_ref = drop.attention_backward_dropout(q64, k64, v64, do64, causal, scale, f32(p), seed,
+                                            offset)
+    Hq, nq, nkv = q.shape[1], q.shape[2], k.shape[2]
+    keep_of = lambda b, h: drop.keep_mask(b * Hq + h, np.arange(nq), nkv, f32(p), seed,  # noqa: E731
+                                          offset)
+    mags = oracle.attention_backward_magnitudes(q64, k64, v64, do64, causal, scale, keep_of,
+                                                drop.keep_scale(f32(p)))
+    check_grads(grads, g_ref, dtype, label, mags=mags)
 
 
 BWD_CASES = [
@@ -187,14 +191,14 @@ def test_backward_dropout_long_sampled():
                                      scale=w.scale)
     torch.cuda.synchronize()
     r = drop.keep_scale(f32(p))
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
     for h in (0, w.Hq - 1):
         z = drop.keep_mask(h, np.arange(w.Nq), w.Nkv, f32(p), seed, offset)
-        g_ref = drop.head_backward_dropout(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]),
-                                           to_f64(do[0, h]), True, w.scale, z, r)
-        for name, g, ref in zip(("dq", "dk", "dv"), (dq[0, h], dk[0, h], dv[0, h]), g_ref):
-            rel = float(np.linalg.norm(to_f64(g) - ref) / np.linalg.norm(ref))
-            say(f"  [long head {h}] {name} Frobenius rel {rel:.3e}")
-            assert rel <= TOL[w.dtype]["grad_rel"], (h, name, rel)
+        args = (to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]), to_f64(do[0, h]), True, w.scale,
+                z, r)
+        g_ref = drop.head_backward_dropout(*args)
+        mags = oracle.head_backward_magnitudes(*args)
+        check_grads((dq[0, h], dk[0, h], dv[0, h]), g_ref, w.dtype, f"long head {h}", mags=mags)
 
 
 @pytest.mark.parametrize("ramp", ["up", "wave"])

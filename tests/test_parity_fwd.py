@@ -13,8 +13,8 @@ import torch
 import exact_attention_115_amd as fa
 import oracle
 from synth import WORKLOADS, make_inputs, random_tensors, to_f64
-from tests.parity_util import (TOL, check_forward, gpu, oracle_heads_forward, run_forward,
-                               sample_heads, say)
+from tests.parity_util import (TOL, all_finite, check_forward, forward_nan_filled, gpu,
+                               oracle_heads_forward, run_forward, sample_heads, say)
 
 pytestmark = [
     pytest.mark.gpu,
@@ -93,18 +93,28 @@ def test_c2_forward(name):
 
 @pytest.mark.parametrize("name", ["c3", "c4", "c5g", "c5m"])
 def test_full_size_forward_sampled_heads(name):
-    """Full-size launch (as timed by the bench); the oracle computes a sample
-    of complete heads, which are independent of the others."""
+    """Full-size launch (as timed by the bench) into NaN-filled outputs:
+    every element must be written and finite. The oracle computes complete
+    heads, which are independent of the others: all 32 heads at c3 (the
+    8-wave, 256-row workgroups over the whole grid), a sample elsewhere."""
     w = WORKLOADS[name]
     say(f"{name}: {w}")
     q, k, v, _ = make_inputs(w, with_grad=False)
-    o, lse = run_forward(q, k, v, w.causal, w.scale)
-    heads = sample_heads(w.B, w.Hq, 2 if w.Nq >= 8192 else 3)
-    o_ref, lse_ref = oracle_heads_forward(q, k, v, w.causal, w.scale, heads)
-    o_s = torch.stack([o[b, h] for b, h in heads])
-    l_s = torch.stack([lse[b, h] for b, h in heads])
-    check_forward(o_s, l_s, o_ref, lse_ref, w.dtype, f"{name} heads {heads}")
-    assert torch.isfinite(o).all()
+    o, lse = forward_nan_filled(gpu(q), gpu(k), gpu(v), w.causal, w.scale)
+    torch.cuda.synchronize()
+    all_finite(f"{name} o", o)
+    all_finite(f"{name} lse", lse)
+    if name == "c3":
+        heads = [(0, h) for h in range(w.Hq)]
+    else:
+        heads = sample_heads(w.B, w.Hq, 2 if w.Nq >= 8192 else 3)
+    o, lse = o.cpu(), lse.cpu()
+    for i in range(0, len(heads), 8):
+        chunk = heads[i:i + 8]
+        o_ref, lse_ref = oracle_heads_forward(q, k, v, w.causal, w.scale, chunk)
+        o_s = torch.stack([o[b, h] for b, h in chunk])
+        l_s = torch.stack([lse[b, h] for b, h in chunk])
+        check_forward(o_s, l_s, o_ref, lse_ref, w.dtype, f"{name} heads {chunk}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -129,13 +139,15 @@ def test_decode_forward(name):
     w = WORKLOADS[name]
     say(f"{name}: {w}")
     q, k, v, _ = make_inputs(w)
-    o, lse = run_forward(q, k, v, w.causal, w.scale)
+    o, lse = forward_nan_filled(gpu(q), gpu(k), gpu(v), w.causal, w.scale)
+    torch.cuda.synchronize()
+    all_finite(f"{name} o", o)
+    all_finite(f"{name} lse", lse)
     heads = [(0, 0), (w.B - 1, w.Hq - 1), (7, 13), (3, 30)]
     o_ref, lse_ref = oracle_heads_forward(q, k, v, w.causal, w.scale, heads)
     o_s = torch.stack([o[b, h] for b, h in heads])
     l_s = torch.stack([lse[b, h] for b, h in heads])
     check_forward(o_s, l_s, o_ref, lse_ref, w.dtype, f"{name} heads {heads}")
-    assert torch.isfinite(o).all()
 
 
 # ------------------------------------------------------------------ edge cases

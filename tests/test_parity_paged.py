@@ -92,16 +92,21 @@ def test_identity_table_equals_contiguous_decode_bitwise():
     assert torch.equal(lse_p, lse_c)
 
 
-def test_out_of_range_entry_reads_zero_page():
-    """A table entry outside [0, num_pages) reads as a page of zeros (no
-    memory access): same result as pointing it at an all-zero page."""
-    B, Hq, Hkv, d, ps = 1, 8, 2, 64, 64
-    q, kp, vp, table, ln = make_case(B, Hq, Hkv, d, ps, [3 * ps], "bf16", seed=64)
+def test_out_of_range_entries_drop_their_keys():
+    """A table entry outside [0, num_pages) (too large or negative) names no
+    page: its keys are dropped from the attention (never read, never scored),
+    against the oracle with those keys removed; a sequence whose every entry
+    is out of range gets O = 0, LSE = -inf."""
+    B, Hq, Hkv, d, ps = 3, 8, 2, 64, 64
+    q, kp, vp, table, ln = make_case(B, Hq, Hkv, d, ps, [3 * ps, 2 * ps + 7, 4 * ps], "bf16",
+                                     seed=64)
     bad = table.copy()
     bad[0, 1] = 1 << 20
+    bad[1, 0] = -5
+    bad[2, :] = kp.shape[0]
     o_bad, lse_bad = run_paged(q, kp, vp, bad, ln, 0.125)
-    kz, vz = kp.clone(), vp.clone()
-    kz[table[0, 1]] = 0
-    vz[table[0, 1]] = 0
-    o_ref, lse_ref = run_paged(q, kz, vz, table, ln, 0.125)
-    assert torch.equal(o_bad, o_ref) and torch.equal(lse_bad, lse_ref)
+    o_ref, lse_ref = oracle.paged_decode_forward(to_f64(q), to_f64(kp), to_f64(vp), bad,
+                                                 ln, 0.125)
+    check_forward(o_bad[:2].cpu(), lse_bad[:2].cpu(), o_ref[:2], lse_ref[:2], "bf16",
+                  "out-of-range entries")
+    assert torch.all(o_bad[2] == 0) and torch.all(torch.isneginf(lse_bad[2]))

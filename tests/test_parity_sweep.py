@@ -59,4 +59,5 @@ def test_random_shape_forward_backward(case):
     o_ref, lse_ref = oracle.attention_forward(q64, k64, v64, causal, scale)
     check_forward(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, label)
     g_ref = oracle.attention_backward(q64, k64, v64, do64, causal, scale)
-    check_grads((dq.cpu(), dk.cpu(), dv.cpu()), g_ref, dtype, label)
+    check_grads((dq.cpu(), dk.cpu(), dv.cpu()), g_ref, dtype, label,
+                mags=oracle.attention_backward_magnitudes(q64, k64, v64, do64, causal, scale))
