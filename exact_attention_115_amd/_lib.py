@@ -24,7 +24,7 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULLPTR", -2: "FA_ERR_SHAPE", -3: "FA_ERR_UNSUPPORTED",
     -4: "FA_ERR_ALIGNMENT", -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_SCALE", -7: "FA_ERR_HIP",
-    -8: "FA_ERR_OVERLAP",
+    -8: "FA_ERR_OVERLAP", -9: "FA_ERR_SCRATCH",
 }
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_stage.argtypes = [i] + bwd
     lib.fa_bwd_stage.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + shape + [f, i, i, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -189,6 +191,13 @@ def fa_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, workspace, scale: 
     """Call fa_bwd_stage on tensors; returns the status code (no exception)."""
     return load().fa_bwd_stage(int(stage), *_bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace,
                                                       scale, causal, stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, stream=None) -> int:
+    """Call fa_bwd_noalloc (the backward on the library's static scratch
+    buffer, no workspace argument); returns the status code (no exception)."""
+    args = _bwd_args(q, k, v, o, lse, do, dq, dk, dv, None, scale, causal, stream)
+    return load().fa_bwd_noalloc(*args[:9], *args[11:])
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor | None:

@@ -30,6 +30,7 @@ SOURCES = [
     "fa_bwd_dq.hip",
     "fa_dropout.hip",
     "fa_fwd_fp8.hip",
+    "fa_noalloc.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

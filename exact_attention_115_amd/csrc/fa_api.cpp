@@ -107,10 +107,12 @@ int check_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
   return FA_OK;
 }
 
+// check_ws = false: the library supplies the workspace itself (it is then
+// neither checked nor part of the overlap checks).
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dO, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, int B,
               int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int causal, int dt,
-              bool* empty, Problem* prob) {
+              bool* empty, Problem* prob, bool check_ws = true) {
   int st = check_shape(B, Hq, Hkv, Nq, Nkv, d, dt, empty);
   if (st != FA_OK) return st;
   if (dt == FA_F32) return FA_ERR_UNSUPPORTED;
@@ -133,7 +135,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   const void* al[9] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : al)
     if (p && !aligned(p, 16)) return FA_ERR_ALIGNMENT;
-  const size_t need = bwd_workspace_bytes(*prob);
+  const size_t need = check_ws ? bwd_workspace_bytes(*prob) : 0;
   if (need > 0) {
     if (!ws) return FA_ERR_NULLPTR;
     if (!aligned(ws, 256)) return FA_ERR_ALIGNMENT;
@@ -242,6 +244,26 @@ size_t bwd_workspace_bytes(const Problem& p) {
   const int gs = bwd_group_split(p);
   if (gs > 1) bytes += 2 * align_up((size_t)gs * kv * sizeof(float), 256);
   return bytes;
+}
+
+int bwd_with_library_workspace(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                               int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,
+                               int causal, fa_dtype dt, hipStream_t stream, LibraryWorkspace get_ws) {
+  bool empty = false;
+  Problem p;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, nullptr, 0, B, Hq, Hkv, Nq, Nkv, d, scale,
+                     causal, dt, &empty, &p, /*check_ws=*/false);
+  if (st != FA_OK || empty) return st;
+  void* ws = nullptr;
+  st = get_ws(bwd_workspace_bytes(p), &ws);
+  if (st != FA_OK) return st;
+  const BwdPtrs t = bwd_ptrs(p, q, k, v, o, lse, dO, dq, dk, dv, ws);
+  for (int stage = 0; stage < 3; ++stage) {
+    st = run_bwd_stage(stage, p, t, stream);
+    if (st != FA_OK) return st;
+  }
+  return FA_OK;
 }
 
 }  // namespace fa
@@ -482,6 +504,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_SCALE: return "scale must be finite and > 0, causal must be 0 or 1";
     case FA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
     case FA_ERR_OVERLAP: return "an output buffer overlaps an input or another output";
+    case FA_ERR_SCRATCH:
+      return "the problem needs more workspace than the library's static scratch buffer holds";
     default: return "unknown status";
   }
 }

@@ -79,6 +79,17 @@ size_t bwd_workspace_bytes(const Problem& p);
 // divisor of G.
 int bwd_group_split(const Problem& p);
 
+// fa_bwd with a workspace the library provides: validates every argument
+// as fa_bwd does (the workspace aside), then calls get_ws(bytes needed,
+// &ptr), which returns FA_OK and a device pointer or an error status, and
+// runs the three backward stages on that workspace. get_ws is called only
+// after the arguments passed the host-side checks.
+typedef int (*LibraryWorkspace)(size_t bytes, void** ws);
+int bwd_with_library_workspace(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                               int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale,
+                               int causal, fa_dtype dt, hipStream_t stream, LibraryWorkspace get_ws);
+
 // Launchers: each enqueues its kernel(s) on `stream` and returns the
 // hipError_t of the launch.
 hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream);

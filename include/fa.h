@@ -70,7 +70,8 @@ enum {
   FA_ERR_WORKSPACE = -5,   /* workspace smaller than fa_*_workspace_size()   */
   FA_ERR_SCALE = -6,       /* scale not finite or not > 0; causal not 0 / 1  */
   FA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch    */
-  FA_ERR_OVERLAP = -8      /* an output overlaps an input                    */
+  FA_ERR_OVERLAP = -8,     /* an output overlaps an input                    */
+  FA_ERR_SCRATCH = -9      /* needs more than the static scratch (fa_bwd_noalloc) */
 };
 
 /* Bytes of device workspace fa_fwd needs for this problem. Zero for prefill
@@ -129,6 +130,29 @@ int fa_bwd_stage(int stage,
                  void* workspace, size_t workspace_bytes,
                  int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                  float scale, int causal, fa_dtype dt, hipStream_t stream);
+
+/* fa_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid allocation). The same computation as fa_bwd, with the same
+ * arguments except the workspace: the library uses its own static device
+ * buffer of FA_NOALLOC_SCRATCH_BYTES bytes per GPU instead, which exists
+ * from the first call on a device until the process ends. Nothing is
+ * allocated or freed by the call (the buffer's address is looked up once
+ * per device, on that device's first call, under a lock).
+ * Limit: problems whose fa_bwd_workspace_size exceeds
+ * FA_NOALLOC_SCRATCH_BYTES return FA_ERR_SCRATCH and enqueue nothing.
+ * Every call on one GPU uses that GPU's one buffer, and the stages of a
+ * call rewrite what they read from it before reading it, so nothing needs
+ * clearing between calls; but two calls that overlap in time on one GPU
+ * (different streams, or host threads enqueuing concurrently) race on the
+ * buffer and must be ordered by the caller. Status codes and execution as
+ * fa_bwd, plus FA_ERR_SCRATCH, and FA_ERR_HIP when the buffer's address
+ * cannot be obtained. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                   float scale, int causal, fa_dtype dt, hipStream_t stream);
 
 /* Decode (one query row per sequence) over a paged K/V cache ([KB]
  * "FlashAttention：为什么少搬数据，反而算得更快" §09 names paged KV as the

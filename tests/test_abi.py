@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert fa.fa_version() >= 100
-    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8]:
+    for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]:
         s = fa.fa_strerror(code)
         assert s and s != "unknown status"
     assert fa.fa_strerror(-99) == "unknown status"
@@ -277,3 +277,29 @@ def test_fwd_fp8_rejects_bad_arguments():
     assert call(q=P(1, 8)) == -4
     assert call(o=P(1)) == -8
     assert call(Nq=0) == 0
+
+
+def bwd_noalloc(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), do=P(6), dq=P(7), dk=P(8), dv=P(9),
+                B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=64, scale=0.125, causal=0, dt=fa.FA_BF16):
+    return fa.load().fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, scale,
+                                    causal, dt, None)
+
+
+def test_bwd_noalloc_rejects_bad_arguments_before_any_hip_call():
+    """fa_bwd_noalloc checks its arguments like fa_bwd (there is no workspace
+    argument) and refuses a problem whose workspace exceeds the static
+    scratch buffer, all before looking the buffer up (no HIP call)."""
+    assert bwd_noalloc(dt=fa.FA_F32) == -3
+    assert bwd_noalloc(do=None) == -1
+    assert bwd_noalloc(dq=P(7, 2)) == -4
+    assert bwd_noalloc(Hq=4, Hkv=3) == -2
+    assert bwd_noalloc(scale=float("nan")) == -6
+    assert bwd_noalloc(dq=P(1)) == -8
+    assert bwd_noalloc(B=0) == 0
+    lib = fa.load()
+    scratch = 32 << 20
+    # 2 float32 row terms per query row: 4 Mi + 64 rows need just over 32 MiB.
+    B, Hq, Hkv, Nq, Nkv, d = 1, 64, 64, 65540, 64, 64
+    assert lib.fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, fa.FA_BF16) > scratch
+    assert bwd_noalloc(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, d=d) == -9
+    assert "static scratch" in fa.fa_strerror(-9)
