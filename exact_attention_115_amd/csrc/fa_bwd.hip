@@ -85,9 +85,29 @@ __device__ __forceinline__ void init_rows(const float* x, int h, f32x16* acc) {
 // that each accumulator stays in the register file its users need: the
 // scores and dP (read by the vector ALU) in vector registers with the
 // stationary K, V operand in accumulation registers (mfma_rows), dK and dV
-// (read once, at the end) in accumulation registers (mfma_acc). The
-// compiler places no hazard waits around these: results are read by other
-// instructions only after xdl_wait().
+// (read once, at the end) in accumulation registers (mfma_acc).
+//
+// The compiler places no wait states around inline assembly, and the
+// hardware does not interlock these hazards of a 32x32x16 product (the wait
+// states are those the compiler's hazard recognizer inserts for the same
+// pairs written with builtins; tests/isa/hazard_rules.hip):
+//   * vector-ALU write of an A / B operand or of the accumulator input, then
+//     the product: 2. The A operands come from LDS (ordered by s_waitcnt);
+//     the B operands of mfma_acc (P, dS) are packed in the step before the
+//     one that uses them; the S / dP accumulators start from LDS loads
+//     (init_rows) and dK / dV from zeros written once, before the loop. The
+//     last tile's products (dkdv_tail), whose P / dS registers the compiler
+//     selects with v_cndmask right before them, use mfma_acc_guarded, which
+//     waits 2 states first.
+//   * the product's result read by any other instruction (or overwritten by
+//     the vector ALU): 12. Scores and dP are read only after xdl_wait()
+//     (24); dK and dV only after the final xdl_wait().
+//   * the result read as the next product's accumulator input, into the
+//     same registers (the chains of S, dP, dK, dV): none.
+// tests/test_isa_hazards.py compiles this file and checks every dK/dV
+// instantiation's assembly against these rules, following the control flow,
+// so that a change of instruction order or register allocation that breaks
+// one of them fails on the CPU.
 template <typename T>
 __device__ __forceinline__ void mfma_rows(f32x16& c, typename T::vec8 a, typename T::vec8& b) {
   // b is tied in and out so that it is used in place, not copied per product.
@@ -102,6 +122,16 @@ __device__ __forceinline__ void mfma_acc(f32x16& c, typename T::vec8 a, typename
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// mfma_acc with two wait states before the product, for call sites where
+// the compiler may write an operand register with a vector-ALU instruction
+// just before (it selects the tail's P / dS registers with v_cndmask).
+template <typename T>
+__device__ __forceinline__ void mfma_acc_guarded(f32x16& c, typename T::vec8 a, typename T::vec8 b) {
+  if constexpr (std::is_same_v<T, BF16>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 // 24 wait states: more than a 32x32x16 product needs before another
 // instruction may read its result.
@@ -261,8 +291,8 @@ __device__ __forceinline__ void dkdv_tail(const uint8_t* qp, const uint8_t* gp, 
     }
 #pragma unroll
     for (int od = 0; od < OD; ++od) {
-      mfma_acc<T>(dv[od], load_kt_dma<T, D>(gp, kt0, kt1, ch, od), as_vec8<T>(wp));
-      mfma_acc<T>(dk[od], load_kt_dma<T, D>(qp, kt0, kt1, ch, od), as_vec8<T>(ws));
+      mfma_acc_guarded<T>(dv[od], load_kt_dma<T, D>(gp, kt0, kt1, ch, od), as_vec8<T>(wp));
+      mfma_acc_guarded<T>(dk[od], load_kt_dma<T, D>(qp, kt0, kt1, ch, od), as_vec8<T>(ws));
     }
   }
 }
