@@ -24,7 +24,19 @@ from __future__ import annotations
 
 import numpy as np
 
-from .reference import head_forward
+from .reference import _softmax_rows, head_forward, visible_mask
+
+# Error of one 8-bit matrix-core product (32x32x64 with E4M3 operands),
+# relative to the sum of the magnitudes of the 64 terms it adds: the
+# products are exact, but their sum is not formed exactly in float32. This
+# constant is a measurement, not a definition: the GPU test
+# test_fp8_score_accumulation_error (tests/test_parity_fp8.py) reads the
+# scores the kernel computes back through the LSE of a one-key softmax and
+# checks that no score is off by more than EPS8 * scale * sum_c |q_c k_c|.
+# Largest seen on MI355X: 2^-12.27 with elements scaled by powers of two
+# from 2^-6 to 2^6, 2^-12.64 over uniformly random codes, 2^-15.6 on N(0, 1)
+# draws; EPS8 leaves a factor of 2.4 over the largest.
+EPS8 = 2.0 ** -11
 
 
 def e4m3_value(code: int) -> float:
@@ -68,10 +80,36 @@ def p_rounding_bound(q8, k8, v8, causal: bool, scale: float, dq: float, dk: floa
     k = decode(k8, dk)
     v = decode(v8, dv)
     nq, nkv = q.shape[0], k.shape[0]
-    from .reference import _softmax_rows, visible_mask
     s = scale * (q @ k.T)
     vis = visible_mask(np.arange(nq), nq, nkv, causal)
     s = np.where(vis, s, -np.inf)
     p, _ = _softmax_rows(s)
     w = np.where(vis, np.maximum(p * 2.0 ** -4, 2.0 ** -10), 0.0)
     return w @ np.abs(v)
+
+
+def accumulation_bound(q8, k8, v8, causal: bool, scale: float, dq: float, dk: float, dv: float,
+                       eps8: float = EPS8):
+    """Bound on what the inexact sums of the 8-bit products can change in O
+    and in the LSE: returns (O bound [N_q, d], LSE bound [N_q]).
+
+    Each score moves by at most E_ij = eps8 * scale * sum_c |q_ic k_jc|.
+    Scores moved by at most E_i = max_j E_ij (over the visible keys) move
+    LSE_i by at most E_i, and every softmax weight by at most a factor
+    exp(+-2 E_i), so O_ic by at most (exp(2 E_i) - 1) sum_j P_ij |V_jc|.
+    The P V products add their terms with the same relative error, at most
+    eps8 times the sum of the magnitudes of the (rounded) terms, which the
+    rounding of P keeps within (1 + 2^-4) sum_j P_ij |V_jc|; the O bound
+    adds that."""
+    q = decode(q8, dq)
+    k = decode(k8, dk)
+    v = decode(v8, dv)
+    nq, nkv = q.shape[0], k.shape[0]
+    vis = visible_mask(np.arange(nq), nq, nkv, causal)
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    p, _ = _softmax_rows(s)
+    e = np.where(vis, eps8 * scale * (np.abs(q) @ np.abs(k).T), 0.0)
+    e_row = e.max(axis=1) if nkv else np.zeros(nq)
+    pv = p @ np.abs(v)
+    o_bound = np.expm1(2.0 * e_row)[:, None] * pv + eps8 * (1.0 + 2.0 ** -4) * pv
+    return o_bound, e_row

@@ -640,3 +640,40 @@ def test_gradient_bound_holds_for_rounded_p_and_ds(dtype, u):
         assert np.all(rows(g - r) <= allow + 1e-15)
         assert np.max(rows(g - r) / (allow + 1e-300)) < 0.5
     assert worst > 0.01
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_accumulation_bound_holds_for_perturbed_scores(causal):
+    """accumulation_bound: moving every score by up to E_ij = eps8 scale
+    sum_c |q_ic k_jc| (random and sign-aligned worst-case moves) and every
+    P V term by up to eps8 of itself keeps O and LSE within the bound; the
+    bound is not vacuous (a sign-aligned move uses a visible part of it)."""
+    rng = np.random.default_rng(92)
+    nq, nkv, d, scale, eps = 24, 90, 32, 0.4, 2.0 ** -6  # a large eps8 makes the effect visible
+    vals = torch.from_numpy(rng.standard_normal((nq + 2 * nkv, d)) * 2).to(torch.float8_e4m3fn)
+    codes = vals.view(torch.uint8).numpy()
+    q8, k8, v8 = codes[:nq], codes[nq:nq + nkv], codes[nq + nkv:]
+    q, k, v = f8.decode(q8), f8.decode(k8), f8.decode(v8)
+    o_ref, lse_ref = f8.head_forward_fp8(q8, k8, v8, causal, scale, 1.0, 1.0, 1.0)
+    o_b, lse_b = f8.accumulation_bound(q8, k8, v8, causal, scale, 1.0, 1.0, 1.0, eps8=eps)
+    vis = oracle.visible_mask(np.arange(nq), nq, nkv, causal)
+    e = eps * scale * (np.abs(q) @ np.abs(k).T)
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    worst = 0.0
+    for trial in range(6):
+        if trial < 3:
+            delta = rng.uniform(-1, 1, e.shape) * e
+        else:  # push the weight towards the keys whose V is largest in column `trial`
+            c = trial - 3
+            delta = np.sign(v[:, c] - o_ref[:, c:c + 1]) * e
+        sp = s + delta
+        m = sp.max(axis=1, keepdims=True)
+        w = np.exp(sp - m)
+        w_sum = w.sum(axis=1, keepdims=True)
+        eta = rng.uniform(-1, 1, (nq, nkv, 1)) * eps
+        o = ((w[:, :, None] * v[None, :, :]) * (1 + eta)).sum(axis=1) / w_sum
+        lse = (m + np.log(w_sum))[:, 0]
+        assert np.all(np.abs(o - o_ref) <= o_b + 1e-12)
+        assert np.all(np.abs(lse - lse_ref) <= lse_b + 1e-12)
+        worst = max(worst, float(np.max(np.abs(o - o_ref) / (o_b + 1e-300))))
+    assert worst > 0.05
