@@ -6,11 +6,14 @@
 // the float32 workloads are small, and this keeps their error at float32
 // rounding (the 16-bit matrix cores would round the operands).
 //
-// One wavefront per workgroup; each lane owns one query row and keeps its
-// scaled query, its online-softmax state (m, l, U) of [KB]
-// "FlashAttention：为什么少搬数据，反而算得更快" §04 and its output row in
-// registers. Key/value tiles of 32 rows are staged in LDS and read by all
-// lanes at the same address (an LDS broadcast).
+// One wavefront per workgroup. Each query row is owned by D / 64 lanes, each
+// holding 64 of its dims: the scaled query, the output row, and (redundantly)
+// the row's online-softmax state (m, l, U) of [KB]
+// "FlashAttention：为什么少搬数据，反而算得更快" §04. A score is the sum of the
+// lanes' partial dot products (one exchange between the two half-waves at
+// d = 128), so every lane keeps 2 x 64 + 32 floats and nothing spills.
+// Key/value tiles of 32 rows are staged in LDS and read by all lanes of a
+// half-wave at the same address (an LDS broadcast).
 #include <math.h>
 
 #include "fa_device.h"
@@ -19,8 +22,8 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;  // query rows per workgroup (one per lane)
 constexpr int kKeys = 32;  // keys per LDS tile
+constexpr int kDims = 64;  // dims per lane
 
 template <int D>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q,
@@ -29,10 +32,14 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
                                                      float* __restrict__ O, float* __restrict__ LSE,
                                                      int Hq, int G, int Nq, int Nkv, float scale,
                                                      int causal) {
+  constexpr int LPR = D / kDims;   // lanes per row
+  constexpr int kRows = 64 / LPR;  // query rows per workgroup
   __shared__ float Ks[kKeys][D];
   __shared__ float Vs[kKeys][D];
 
   const int lane = threadIdx.x;
+  const int part = lane / kRows;   // which 64 dims of the row
+  const int c0 = part * kDims;
   const int ntiles = (Nq + kRows - 1) / kRows;
   const int tile = blockIdx.x % ntiles;
   const int bh = blockIdx.x / ntiles;
@@ -40,17 +47,17 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   const int b = bh / Hq;
   const int hkv = hq / G;
   const int Hkv = Hq / G;
-  const int row = tile * kRows + lane;
+  const int row = tile * kRows + lane % kRows;
   const int offset = Nkv - Nq;  // causal: key j visible to row i iff j <= i + offset
 
   const size_t qbase = ((size_t)(b * Hq + hq) * Nq) * D;
   const size_t kbase = ((size_t)(b * Hkv + hkv) * Nkv) * D;
 
-  float q[D];
-  float u[D];
+  float q[kDims];
+  float u[kDims];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    q[c] = row < Nq ? Q[qbase + (size_t)row * D + c] * scale : 0.0f;
+  for (int c = 0; c < kDims; ++c) {
+    q[c] = row < Nq ? Q[qbase + (size_t)row * D + c0 + c] * scale : 0.0f;
     u[c] = 0.0f;
   }
   float m = -INFINITY;
@@ -79,7 +86,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
       const int key = k0 + j;
       float acc = 0.0f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc = fmaf(q[c], Ks[j][c], acc);
+      for (int c = 0; c < kDims; ++c) acc = fmaf(q[c], Ks[j][c0 + c], acc);
+      if constexpr (LPR == 2) acc += __shfl_xor(acc, 32, 64);  // the other half's dims
       const bool vis = key < Nkv && (!causal || key <= row + offset);
       s[j] = vis ? acc : -INFINITY;
       mt = fmaxf(mt, s[j]);
@@ -89,13 +97,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
     const float a = (m == -INFINITY) ? 0.0f : expf(m - m_new);
     l *= a;
 #pragma unroll
-    for (int c = 0; c < D; ++c) u[c] *= a;
+    for (int c = 0; c < kDims; ++c) u[c] *= a;
 #pragma unroll 4
     for (int j = 0; j < kKeys; ++j) {
       const float p = expf(s[j] - m_new);
       l += p;
 #pragma unroll
-      for (int c = 0; c < D; ++c) u[c] = fmaf(p, Vs[j][c], u[c]);
+      for (int c = 0; c < kDims; ++c) u[c] = fmaf(p, Vs[j][c0 + c], u[c]);
     }
     m = m_new;
   }
@@ -103,14 +111,15 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   if (row >= Nq) return;
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-  for (int c = 0; c < D; ++c) O[qbase + (size_t)row * D + c] = u[c] * inv;
-  LSE[(size_t)(b * Hq + hq) * Nq + row] = l > 0.0f ? m + logf(l) : -INFINITY;
+  for (int c = 0; c < kDims; ++c) O[qbase + (size_t)row * D + c0 + c] = u[c] * inv;
+  if (part == 0) LSE[(size_t)(b * Hq + hq) * Nq + row] = l > 0.0f ? m + logf(l) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const Problem& p, const FwdPtrs& t, hipStream_t stream) {
-  dim3 grid(((p.Nq + kRows - 1) / kRows) * p.Hq * p.B);
+  const int rows = 64 / (p.d / kDims);  // query rows per workgroup
+  dim3 grid(((p.Nq + rows - 1) / rows) * p.Hq * p.B);
   dim3 block(64);
   const float* q = static_cast<const float*>(t.q);
   const float* k = static_cast<const float*>(t.k);

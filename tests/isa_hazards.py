@@ -33,6 +33,7 @@ the nearest write over all incoming paths.
 
 from __future__ import annotations
 
+import functools
 import os
 import re
 import subprocess
@@ -58,6 +59,30 @@ def compile_to_asm(src: str, include_dirs, extra_flags=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed: {' '.join(cmd)}\n{r.stderr[-4000:]}")
     return r.stdout
+
+
+@functools.lru_cache(maxsize=None)
+def library_asm(name: str) -> str:
+    """gfx950 assembly of one of the library's sources (cached per process)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "exact_attention_115_amd", "csrc")
+    return compile_to_asm(os.path.join(csrc, name), [os.path.join(root, "include"), csrc])
+
+
+def kernel_resources(asm: str) -> dict:
+    """Kernel name -> its code-object metadata entries (vgpr_count,
+    vgpr_spill_count, sgpr_spill_count, private_segment_fixed_size,
+    group_segment_fixed_size) as ints."""
+    out = {}
+    for block in asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        vals = {}
+        for key in ("vgpr_count", "vgpr_spill_count", "sgpr_spill_count",
+                    "private_segment_fixed_size", "group_segment_fixed_size"):
+            m = re.search(r"\.%s:\s+(\d+)" % key, block)
+            vals[key] = int(m.group(1)) if m else None
+        out[name] = vals
+    return out
 
 
 def functions(asm: str) -> dict:

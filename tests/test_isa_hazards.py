@@ -83,7 +83,7 @@ def test_checker_flags_the_probes_without_their_wait_states(probe_functions):
 
 
 def test_dkdv_kernels_have_no_matrix_core_hazards():
-    fns = H.functions(H.compile_to_asm(os.path.join(CSRC, "fa_bwd.hip"), INC))
+    fns = H.functions(H.library_asm("fa_bwd.hip"))
     kernels = {n: l for n, l in fns.items() if "bwd_dkdv_kernel" in n}
     assert len(kernels) == 16  # {bf16, f16} x {64, 128} x causal x dropout
     bad = {n: H.check(l) for n, l in kernels.items()}

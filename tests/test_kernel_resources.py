@@ -1,0 +1,32 @@
+"""Every kernel of the library compiles for gfx950 without register spills
+and without scratch memory (CPU only: hipcc cross-compiles the sources to
+assembly and the test reads the code-object metadata). A spill would put
+per-lane state in memory inside the hot loops."""
+
+import concurrent.futures as cf
+import os
+import shutil
+
+import pytest
+
+from exact_attention_115_amd import build as B
+from tests import isa_hazards as H
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.HIPCC) and not shutil.which("hipcc"),
+                                reason="needs hipcc")
+
+KERNEL_SOURCES = [s for s in B.SOURCES if s.endswith(".hip")]
+
+
+def test_no_kernel_spills_or_uses_scratch():
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(KERNEL_SOURCES))) as ex:
+        asms = dict(zip(KERNEL_SOURCES, ex.map(H.library_asm, KERNEL_SOURCES)))
+    bad, count = [], 0
+    for src, asm in asms.items():
+        for name, r in H.kernel_resources(asm).items():
+            count += 1
+            if r["vgpr_spill_count"] or r["private_segment_fixed_size"]:
+                bad.append(f"{src}: {name}: {r}")
+    print(f"{count} kernels checked")
+    assert count >= 80
+    assert not bad, "\n".join(bad)
