@@ -59,7 +59,12 @@
 extern "C" {
 #endif
 
-typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+/* Element type of q, k, v and the 16-bit outputs. fa_dtype is a plain int
+ * (not the enum type) so that any value a caller passes is a defined value
+ * of the parameter; the library rejects values other than these three with
+ * FA_ERR_UNSUPPORTED. */
+enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 };
+typedef int fa_dtype;
 
 enum {
   FA_OK = 0,

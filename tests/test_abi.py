@@ -15,6 +15,14 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH), reason="libfa.so not built")
 
+# The library the checks below call: libfa.so through ctypes, unless another
+# module (test_abi_sanitized.py) installs a stand-in with the same entry points.
+BACKEND = {"lib": None}
+
+
+def lib():
+    return BACKEND["lib"] or fa.load()
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -32,11 +40,11 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert fa.fa_version() >= 100
+    assert lib().fa_version() >= 100
     for code in [0, -1, -2, -3, -4, -5, -6, -7, -8, -9]:
-        s = fa.fa_strerror(code)
+        s = lib().fa_strerror(code).decode()
         assert s and s != "unknown status"
-    assert fa.fa_strerror(-99) == "unknown status"
+    assert lib().fa_strerror(-99).decode() == "unknown status"
 
 
 def _align(x, a=256):
@@ -44,32 +52,32 @@ def _align(x, a=256):
 
 
 def test_workspace_sizes():
-    lib = fa.load()
+    lib_ = lib()
     # Prefill forward needs none; float32 needs none.
-    assert lib.fa_fwd_workspace_size(1, 32, 32, 4096, 4096, 128, fa.FA_BF16) == 0
-    assert lib.fa_fwd_workspace_size(1, 1, 1, 1, 256, 64, fa.FA_F32) == 0
+    assert lib_.fa_fwd_workspace_size(1, 32, 32, 4096, 4096, 128, fa.FA_BF16) == 0
+    assert lib_.fa_fwd_workspace_size(1, 1, 1, 1, 256, 64, fa.FA_F32) == 0
     # Decode: per split one float32 row (d values) plus one LSE per query head.
-    ws = lib.fa_fwd_workspace_size(16, 32, 8, 1, 8192, 128, fa.FA_BF16)
+    ws = lib_.fa_fwd_workspace_size(16, 32, 8, 1, 8192, 128, fa.FA_BF16)
     assert ws > 0 and ws % 256 == 0
     rows = ws // (129 * 4)
     assert rows % (16 * 32) == 0
     # Backward: the float32 row terms D and LSE log2(e), linear in N.
     for B, Hq, Hkv, N, d in [(1, 32, 32, 4096, 128), (2, 16, 16, 1024, 64), (4, 32, 8, 2048, 128)]:
         want = 2 * _align(B * Hq * N * 4)
-        assert lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) == want
+        assert lib_.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) == want
     # MQA with few key blocks: the head group is split over s workgroups, which
     # adds float32 partial dK and dV planes (s of each), s a divisor of G.
     B, Hq, Hkv, N, d = 4, 32, 1, 2048, 128
     base = 2 * _align(B * Hq * N * 4)
-    extra = lib.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) - base
+    extra = lib_.fa_bwd_workspace_size(B, Hq, Hkv, N, N, d, fa.FA_BF16) - base
     plane = B * Hkv * N * d * 4
     assert extra > 0 and extra % (2 * plane) == 0
     s = extra // (2 * plane)
     assert s > 1 and (Hq // Hkv) % s == 0
-    assert lib.fa_bwd_workspace_size(1, 1, 1, 10, 10, 64, fa.FA_F32) == 0
+    assert lib_.fa_bwd_workspace_size(1, 1, 1, 10, 10, 64, fa.FA_F32) == 0
     # Invalid problems report 0.
-    assert lib.fa_bwd_workspace_size(1, 3, 2, 10, 10, 64, fa.FA_BF16) == 0
-    assert lib.fa_fwd_workspace_size(1, 2, 2, 1, 10, 96, fa.FA_BF16) == 0
+    assert lib_.fa_bwd_workspace_size(1, 3, 2, 10, 10, 64, fa.FA_BF16) == 0
+    assert lib_.fa_fwd_workspace_size(1, 2, 2, 1, 10, 96, fa.FA_BF16) == 0
 
 
 # Fake, 256-byte aligned, never dereferenced device addresses: every call below
@@ -83,7 +91,7 @@ def P(i, off=0):
 
 def fwd(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), ws=None, ws_bytes=0, B=1, Hq=2, Hkv=2, Nq=64,
         Nkv=64, d=64, scale=0.125, causal=0, dt=fa.FA_BF16):
-    return fa.load().fa_fwd(q, k, v, o, lse, ws, ws_bytes, B, Hq, Hkv, Nq, Nkv, d, scale, causal,
+    return lib().fa_fwd(q, k, v, o, lse, ws, ws_bytes, B, Hq, Hkv, Nq, Nkv, d, scale, causal,
                             dt, None)
 
 
@@ -93,8 +101,8 @@ def bwd(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), do=P(6), dq=P(7), dk=P(8), dv=
     args = (q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, Hq, Hkv, Nq, Nkv, d, scale, causal, dt,
             None)
     if stage is None:
-        return fa.load().fa_bwd(*args)
-    return fa.load().fa_bwd_stage(stage, *args)
+        return lib().fa_bwd(*args)
+    return lib().fa_bwd_stage(stage, *args)
 
 
 def test_fwd_rejects_bad_arguments():
@@ -133,7 +141,7 @@ def test_size_limits_are_enforced():
 
 def test_fwd_decode_needs_workspace():
     assert fwd(Nq=1, Nkv=8192, ws=None) == -1
-    need = fa.load().fa_fwd_workspace_size(1, 2, 2, 1, 8192, 64, fa.FA_BF16)
+    need = lib().fa_fwd_workspace_size(1, 2, 2, 1, 8192, 64, fa.FA_BF16)
     assert fwd(Nq=1, Nkv=8192, ws=P(10), ws_bytes=need - 1) == -5
     assert fwd(Nq=1, Nkv=8192, ws=P(10, 16), ws_bytes=need) == -4
 
@@ -149,7 +157,7 @@ def test_bwd_rejects_bad_arguments():
     assert bwd(do=None) == -1
     assert bwd(dk=None) == -1
     assert bwd(ws=None) == -1
-    need = fa.load().fa_bwd_workspace_size(1, 2, 2, 64, 64, 64, fa.FA_BF16)
+    need = lib().fa_bwd_workspace_size(1, 2, 2, 64, 64, 64, fa.FA_BF16)
     assert need > 0 and bwd(ws_bytes=need - 1) == -5
     assert bwd(ws=P(10, 64)) == -4
     assert bwd(dq=P(7, 2)) == -4
@@ -166,17 +174,17 @@ def test_bwd_rejects_bad_arguments():
 def paged(q=P(1), kp=P(2), vp=P(3), table=P(4), lens=P(5), o=P(6), lse=P(7), ws=P(8),
           ws_bytes=1 << 30, B=2, Hq=4, Hkv=2, num_pages=8, page_size=64, max_pages=4, d=64,
           scale=0.125, dt=fa.FA_BF16):
-    return fa.load().fa_fwd_paged(q, kp, vp, table, lens, o, lse, ws, ws_bytes, B, Hq, Hkv,
+    return lib().fa_fwd_paged(q, kp, vp, table, lens, o, lse, ws, ws_bytes, B, Hq, Hkv,
                                   num_pages, page_size, max_pages, d, scale, dt, None)
 
 
 def test_paged_workspace_matches_contiguous_decode():
-    lib = fa.load()
+    lib_ = lib()
     for B, Hq, Hkv, ps, mp, d in [(16, 32, 8, 128, 64, 128), (3, 8, 2, 64, 20, 64), (2, 32, 1, 256, 8, 128)]:
-        want = lib.fa_fwd_workspace_size(B, Hq, Hkv, 1, ps * mp, d, fa.FA_BF16)
-        assert lib.fa_fwd_paged_workspace_size(B, Hq, Hkv, ps, mp, d, fa.FA_BF16) == want > 0
-    assert lib.fa_fwd_paged_workspace_size(2, 4, 2, 96, 4, 64, fa.FA_BF16) == 0   # page size
-    assert lib.fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_F32) == 0    # dtype
+        want = lib_.fa_fwd_workspace_size(B, Hq, Hkv, 1, ps * mp, d, fa.FA_BF16)
+        assert lib_.fa_fwd_paged_workspace_size(B, Hq, Hkv, ps, mp, d, fa.FA_BF16) == want > 0
+    assert lib_.fa_fwd_paged_workspace_size(2, 4, 2, 96, 4, 64, fa.FA_BF16) == 0   # page size
+    assert lib_.fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_F32) == 0    # dtype
 
 
 def test_paged_rejects_bad_arguments():
@@ -194,7 +202,7 @@ def test_paged_rejects_bad_arguments():
     assert paged(lens=P(5, 2)) == -4          # int32 array not 4-byte aligned
     assert paged(q=P(1, 8)) == -4
     assert paged(ws=P(8, 16)) == -4
-    need = fa.load().fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_BF16)
+    need = lib().fa_fwd_paged_workspace_size(2, 4, 2, 64, 4, 64, fa.FA_BF16)
     assert paged(ws_bytes=need - 1) == -5
     assert paged(scale=0.0) == -6
     assert paged(o=P(1)) == -8                # output aliases q
@@ -206,7 +214,7 @@ def fwd_drop(p=0.1, seed=1, offset=0, **kw):
     a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), ws=None, ws_bytes=0, B=1, Hq=2, Hkv=2,
              Nq=64, Nkv=64, d=64, scale=0.125, causal=0, dt=fa.FA_BF16)
     a.update(kw)
-    return fa.load().fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"],
+    return lib().fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"],
                                     a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"],
                                     a["d"], a["scale"], a["causal"], p, seed, offset, a["dt"], None)
 
@@ -225,24 +233,24 @@ def test_fwd_dropout_rejects_bad_arguments():
 
 
 def test_dropout_mask_rejects_bad_arguments():
-    lib = fa.load()
-    assert lib.fa_dropout_mask(P(1), 1, 2, 3, 4, 1.0, 1, 0, None) == -6
-    assert lib.fa_dropout_mask(P(1), 1, 2, 3, 4, float("nan"), 1, 0, None) == -6
-    assert lib.fa_dropout_mask(P(1), -1, 2, 3, 4, 0.5, 1, 0, None) == -2
-    assert lib.fa_dropout_mask(None, 1, 2, 3, 4, 0.5, 1, 0, None) == -1
-    assert lib.fa_dropout_mask(None, 1, 2, 0, 4, 0.5, 1, 0, None) == 0
-    assert lib.fa_dropout_mask(P(1), 1 << 16, 1 << 16, 1, 1, 0.5, 1, 0, None) == -3
+    lib_ = lib()
+    assert lib_.fa_dropout_mask(P(1), 1, 2, 3, 4, 1.0, 1, 0, None) == -6
+    assert lib_.fa_dropout_mask(P(1), 1, 2, 3, 4, float("nan"), 1, 0, None) == -6
+    assert lib_.fa_dropout_mask(P(1), -1, 2, 3, 4, 0.5, 1, 0, None) == -2
+    assert lib_.fa_dropout_mask(None, 1, 2, 3, 4, 0.5, 1, 0, None) == -1
+    assert lib_.fa_dropout_mask(None, 1, 2, 0, 4, 0.5, 1, 0, None) == 0
+    assert lib_.fa_dropout_mask(P(1), 1 << 16, 1 << 16, 1, 1, 0.5, 1, 0, None) == -3
 
 
 def test_bwd_dropout_rejects_bad_arguments():
-    lib = fa.load()
+    lib_ = lib()
 
     def call(p=0.1, **kw):
         a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), do=P(6), dq=P(7), dk=P(8), dv=P(9),
                  ws=P(10), ws_bytes=1 << 30, B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=64, scale=0.125,
                  causal=0, dt=fa.FA_BF16)
         a.update(kw)
-        return lib.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+        return lib_.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
                                   a["dk"], a["dv"], a["ws"], a["ws_bytes"], a["B"], a["Hq"],
                                   a["Hkv"], a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], p,
                                   7, 0, a["dt"], None)
@@ -257,13 +265,13 @@ def test_bwd_dropout_rejects_bad_arguments():
 
 
 def test_fwd_fp8_rejects_bad_arguments():
-    lib = fa.load()
+    lib_ = lib()
 
     def call(**kw):
         a = dict(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=128,
                  scale=0.1, causal=0, dq=1.0, dk=1.0, dv=1.0)
         a.update(kw)
-        return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+        return lib_.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                               a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], a["dq"], a["dk"],
                               a["dv"], None)
 
@@ -281,7 +289,7 @@ def test_fwd_fp8_rejects_bad_arguments():
 
 def bwd_noalloc(q=P(1), k=P(2), v=P(3), o=P(4), lse=P(5), do=P(6), dq=P(7), dk=P(8), dv=P(9),
                 B=1, Hq=2, Hkv=2, Nq=64, Nkv=64, d=64, scale=0.125, causal=0, dt=fa.FA_BF16):
-    return fa.load().fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, scale,
+    return lib().fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, scale,
                                     causal, dt, None)
 
 
@@ -296,10 +304,10 @@ def test_bwd_noalloc_rejects_bad_arguments_before_any_hip_call():
     assert bwd_noalloc(scale=float("nan")) == -6
     assert bwd_noalloc(dq=P(1)) == -8
     assert bwd_noalloc(B=0) == 0
-    lib = fa.load()
+    lib_ = lib()
     scratch = 32 << 20
     # 2 float32 row terms per query row: 4 Mi + 64 rows need just over 32 MiB.
     B, Hq, Hkv, Nq, Nkv, d = 1, 64, 64, 65540, 64, 64
-    assert lib.fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, fa.FA_BF16) > scratch
+    assert lib_.fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, fa.FA_BF16) > scratch
     assert bwd_noalloc(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, d=d) == -9
-    assert "static scratch" in fa.fa_strerror(-9)
+    assert "static scratch" in lib_.fa_strerror(-9).decode()
