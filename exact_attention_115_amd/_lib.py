@@ -46,7 +46,14 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with exact_attention_115_amd.build.build() "
             "(there is no fallback implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at ``path`` with the C signatures of
+    include/fa.h declared (load() uses it for libfa.so)."""
+    lib = ctypes.CDLL(path)
     vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     shape = [i, i, i, i, i, i]
     lib.fa_fwd_workspace_size.argtypes = shape + [i]
@@ -79,7 +86,6 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + shape + [f, i, f, f, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_dropout_mask.restype = i
-    _lib = lib
     return lib
 
 

@@ -2,7 +2,11 @@
 
 Every call compiles every source again (the build check must really build).
 Objects are compiled in parallel and linked into
-``exact_attention_115_amd/libfa.so``.
+``exact_attention_115_amd/libfa.so``. The same sources are also built with
+-DFA_STAGE_BARRIERS into ``libfa_stagesync.so``, the debug build whose
+kernels wait for every copy and meet at a barrier between the copy and the
+compute of each pipeline step; the tests check that it gives bit-identical
+results. Nothing but the tests loads it.
 """
 
 from __future__ import annotations
@@ -19,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+STAGESYNC_LIB = os.path.join(PKG, "libfa_stagesync.so")
 
 ARCH = "gfx950"
 SOURCES = [
@@ -50,31 +55,46 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+VARIANTS = {LIB: [], STAGESYNC_LIB: ["-DFA_STAGE_BARRIERS"]}
+
+
+def _compile(job) -> str:
+    src, out_dir, defines = job
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *defines, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link libfa.so; returns the library path."""
-    if os.path.isdir(BUILD):
-        shutil.rmtree(BUILD)
-    os.makedirs(BUILD)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources, link libfa.so and the stage-barrier debug
+    library; returns the path of libfa.so."""
+    if os.path.isdir(BUILD):
+        shutil.rmtree(BUILD)
+    jobs = []
+    for lib, defines in VARIANTS.items():
+        out_dir = os.path.join(BUILD, os.path.splitext(os.path.basename(lib))[0])
+        os.makedirs(out_dir)
+        jobs += [(src, out_dir, defines) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n = len(SOURCES)
+    for i, lib in enumerate(VARIANTS):
+        _link(lib, objs[i * n:(i + 1) * n])
+        if verbose:
+            print(f"built {lib}")
     return LIB
 
 

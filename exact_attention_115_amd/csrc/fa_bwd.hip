@@ -509,6 +509,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
     tile_rows<T, D>(qs0, kr0, kr1, kf, ls0, h, sa);
     tile_rows<T, D>(gs0, kr0, kr1, vf, ds0, h, da);
     load_tile(2, 2);
+    FA_STAGE_SYNC();
     const uint32_t kwt = keep_word(0);
     xdl_wait();
     mask_tile(0, sa);
@@ -529,6 +530,7 @@ __global__ __launch_bounds__(NTB, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int i = i0 + r;
       if (i < total) {
         load_tile(i + 2, (r + 3) & 3);
+        FA_STAGE_SYNC();
         f32x16* s = even ? sa : sb;
         f32x16* dpc = even ? da : db;
         const uint32_t kwt = keep_word(i);

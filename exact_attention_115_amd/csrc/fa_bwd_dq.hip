@@ -267,10 +267,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(DqArgs a) {
   __syncthreads();
   for (int j = 0; j < n_tiles; j += 2) {
     load_kv(j + 1, kbuf1, vbuf1);
+    FA_STAGE_SYNC();
     if (j < n_w) compute(j, kbuf0, vbuf0);
     __syncthreads();
     if (j + 1 < n_tiles) {
       load_kv(j + 2, kbuf0, vbuf0);
+      FA_STAGE_SYNC();
       if (j + 1 < n_w) compute(j + 1, kbuf1, vbuf1);
       __syncthreads();
     }

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
   const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
   load_k(wave);
   load_v(wave);
+  FA_STAGE_WAIT();
   wait_copies<2 * CPT>();  // this wave's Q blocks
   __syncthreads();         // everyone's Q blocks
 
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
     // the split fill zeros, so every pass issues the same copies).
     wait_copies<CPT>();
     load_k(j + 4);
+    FA_STAGE_WAIT();
     // Keys past the end and, paged, every key of a tile whose table entry
     // is out of range: such keys are dropped, not read as zeros.
     const int key_lim = (PAGED && tile_page(j) < 0) ? key0 : key_end;
@@ -323,6 +325,7 @@ __global__ __launch_bounds__(NT, 1) void decode_split_kernel(DecArgs a) {
     }
     wait_copies<CPT>();
     load_v(j + 4);
+    FA_STAGE_WAIT();
   }
   // Copies past the split may still be in flight.
   wait_copies<0>();

@@ -11,6 +11,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Stage barriers of the debug build (compiled with -DFA_STAGE_BARRIERS).
+// FA_STAGE_WAIT waits for every memory operation the wave has in flight;
+// FA_STAGE_SYNC does that and then a workgroup barrier. The pipelined
+// kernels place FA_STAGE_SYNC between a step's copy issue and its compute
+// (and in every round that only copies, so all waves meet it equally
+// often); the decode kernel, whose waves pipeline independently, places
+// FA_STAGE_WAIT after each copy issue. Both change only when data arrives,
+// never what is computed, so the debug build must give bit-identical
+// results: a difference exposes a buffer read before its copy landed, or
+// overwritten while it was still being read. In the normal build both are
+// empty.
+#ifdef FA_STAGE_BARRIERS
+#define FA_STAGE_WAIT()                \
+  do {                                 \
+    asm volatile("" ::: "memory");     \
+    __builtin_amdgcn_s_waitcnt(0);     \
+  } while (0)
+#define FA_STAGE_SYNC() \
+  do {                  \
+    FA_STAGE_WAIT();    \
+    __syncthreads();    \
+  } while (0)
+#else
+#define FA_STAGE_WAIT() ((void)0)
+#define FA_STAGE_SYNC() ((void)0)
+#endif
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

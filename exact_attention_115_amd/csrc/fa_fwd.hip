@@ -394,6 +394,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
       if (i < n_w) {
         load_k(i + 3, kslot(r ^ 1));
         load_v(i + 1, vslot(r ^ 1));
+        FA_STAGE_SYNC();
         if constexpr (r == 0)
           step(i, sb, pa, sa, pb, kslot(0), vslot(0));
         else
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_mfma_kernel(FwdArgs a) {
   for (int i = n_w; i < n_tiles; ++i) {
     load_k(i + 3, kslot((i + 1) & 1));
     load_v(i + 1, vslot((i + 1) & 1));
+    FA_STAGE_SYNC();
     __syncthreads();
   }
 

@@ -30,3 +30,26 @@ def test_no_kernel_spills_or_uses_scratch():
     print(f"{count} kernels checked")
     assert count >= 80
     assert not bad, "\n".join(bad)
+
+
+def _count(asm, needle):
+    return sum(1 for line in asm.splitlines() if line.strip().startswith(needle))
+
+
+@pytest.mark.parametrize("src,needle", [("fa_fwd.hip", "s_barrier"), ("fa_bwd.hip", "s_barrier"),
+                                        ("fa_bwd_dq.hip", "s_barrier"),
+                                        ("fa_fwd_fp8.hip", "s_barrier"),
+                                        ("fa_decode.hip", "s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)")])
+def test_stage_barrier_build_adds_its_waits(src, needle):
+    """The debug build (-DFA_STAGE_BARRIERS, compared bit for bit with the
+    normal build by the GPU tests) really adds barriers, or full waits in
+    the decode kernel, and still spills nothing."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    normal = H.library_asm(src)
+    debug = H.compile_to_asm(os.path.join(B.CSRC, src), [os.path.join(root, "include"), B.CSRC],
+                             ["-DFA_STAGE_BARRIERS"])
+    n0, n1 = _count(normal, needle), _count(debug, needle)
+    print(f"{src}: {needle}: {n0} -> {n1}")
+    assert n1 > n0
+    for name, r in H.kernel_resources(debug).items():
+        assert not r["vgpr_spill_count"] and not r["private_segment_fixed_size"], (name, r)
