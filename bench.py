@@ -26,6 +26,14 @@ wall time (default 150; 0 turns it off), so that a short warm-up (say 5
 steps) does not leave the clock still rising inside the timed region. The
 settle time and the number of steps it ran are reported in the JSON line.
 
+Timing: the K timed steps run back to back between two events (no event
+between kernels), bracketed by synchronizations; ``ms_per_step`` and
+``value`` come from that region. A second region of K steps, right after it,
+records an event after every kernel and gives each kernel's average launch
+duration (``kernel_ms``, the roofline objects). Event records between
+kernels add a few microseconds each, so they are kept out of the step time.
+Decode workloads time each call between its own events instead (see below).
+
 Prints ONE JSON line. ``--workload`` selects another synthetic workload for
 development measurements (decode workloads report HBM GB/s, each timed call
 starting from cold caches unless --warm-cache).
@@ -362,12 +370,18 @@ def main():
     for i in range(args.steps):
         if cold:
             flush.fill_(i & 0xFF)
-        step(evs[i])
+        step(evs[i] if cold else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+    if not cold:
+        # Per-kernel durations: a second region of K steps with an event
+        # after every kernel.
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
     per_kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
                      for j, n in enumerate(names)}
     if w.Nq == 1:
