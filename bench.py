@@ -161,6 +161,18 @@ def read_traffic(kernel_key):
     return float(m_bytes.group(1))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s):
     """Time the float64 oracle (as it stands) on a bounded sample of whole
     heads of the workload; returns the throughput in the bench's unit."""
@@ -190,10 +202,11 @@ def cpu_baseline(w, budget_s):
     if w.Nq == 1:
         nbytes = decode_bytes(w) * done / (w.B * w.Hq)
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+                "cpu": cpu_model(), "host_cpus": os.cpu_count(),
                 "sample": f"{done} of {w.B * w.Hq} (batch, head) rows of {w.name}, forward, "
                           f"float64 numpy, {dt:.1f} s"}
     return {"value": per_head_flop * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{done} of {w.B * w.Hq} heads of {w.name} "
                       f"({'forward + backward' if w.backward else 'forward'}), float64 numpy, "
                       f"{dt:.1f} s; algorithmic FLOP counted as on the GPU"}
@@ -382,8 +395,8 @@ def main():
         for i in range(args.steps):
             step(evs[i])
         torch.cuda.synchronize()
-    per_kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-                     for j, n in enumerate(names)}
+    per_call = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    per_kernel_ms = {n: sum(t) / args.steps for n, t in per_call.items()}
     if w.Nq == 1:
         # Decode: time per call between its own events. From cold caches the
         # flushes are not counted; with warm caches a call (about 20 us at
@@ -422,6 +435,8 @@ def main():
                    "N_kv": w.Nkv, "d": w.d, "causal": w.causal, "parallelism": "single GPU"},
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel_ms.items()},
+        "kernel_ms_median": {n: round(t[len(t) // 2], 4) for n, t in per_call.items()},
+        "kernel_ms_min": {n: round(t[0], 4) for n, t in per_call.items()},
     }
     if w.Nq == 1:
         # Decode: HBM-bound, reported as algorithmic bytes per second.
