@@ -200,9 +200,10 @@ int run_bwd_stage(int stage, const Problem& p, const BwdPtrs& t, hipStream_t str
 }  // namespace
 
 DecodeSplit decode_split(const Problem& p) {
-  // One workgroup per CU (each keeps three 64-key tiles of K and V in
-  // flight): split the key range so that about 256 workgroups cover all
-  // (b, kv head, query-head group) units, with at least two tiles per split.
+  // One workgroup per CU (its LDS holds a private 64-key K tile and V tile
+  // for each of its four waves, each refilled as soon as it has been read):
+  // split the key range so that about 256 workgroups cover all (b, kv head,
+  // query-head group) units, with at least two tiles per split.
   const long long units = (long long)p.B * p.Hkv * ((p.G + 31) / 32);
   const int tiles = (p.Nkv + 63) / 64;
   long long want = units > 0 ? (256 + units - 1) / units : 1;
