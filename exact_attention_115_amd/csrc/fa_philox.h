@@ -25,19 +25,27 @@ struct DropParams {
   float rscale;    // 256 / (256 - theta)
 };
 
+// The 128-bit product a * b: returns its low 64 bits and stores the high
+// 64 bits in *hi. Both halves come from the same four 32 x 32 -> 64 partial
+// products (a = a1 2^32 + a0, b = b1 2^32 + b0), each a multiply-add of two
+// 32-bit values into a 64-bit one that cannot overflow.
+__host__ __device__ __forceinline__ uint64_t mulhilo64(uint64_t a, uint64_t b, uint64_t* hi) {
+  const uint64_t a0 = (uint32_t)a, a1 = a >> 32, b0 = (uint32_t)b, b1 = b >> 32;
+  const uint64_t p00 = a0 * b0;
+  const uint64_t p01 = a0 * b1 + (p00 >> 32);
+  const uint64_t p10 = a1 * b0 + (uint32_t)p01;
+  *hi = a1 * b1 + (p01 >> 32) + (p10 >> 32);
+  return (p10 << 32) | (uint32_t)p00;
+}
+
 // The four output words of Philox4x64-10 for counter c and key (k0, k1).
 __host__ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint64_t hi0 = __umul64hi(M0, c[0]), hi1 = __umul64hi(M1, c[2]);
-#else
-    const uint64_t hi0 = (uint64_t)(((unsigned __int128)M0 * c[0]) >> 64);
-    const uint64_t hi1 = (uint64_t)(((unsigned __int128)M1 * c[2]) >> 64);
-#endif
-    const uint64_t lo0 = M0 * c[0], lo1 = M1 * c[2];
+    uint64_t hi0, hi1;
+    const uint64_t lo0 = mulhilo64(M0, c[0], &hi0), lo1 = mulhilo64(M1, c[2], &hi1);
     const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
