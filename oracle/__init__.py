@@ -46,9 +46,11 @@ of each sequence gathered through its page-table row, then the definition.
 
 Readings of the pages where they are silent are listed in ``reference``.
 Parity status: every function here is pinned by a CPU test in
-``tests/test_oracle.py``; the only unpinned convention is the output of a
-query row that sees no key at all (O = 0, LSE = -inf), which the pages leave
-open ([KB] §04 says only that such rows must be handled).
+``tests/test_oracle.py``. The one unpinned value is the output O = 0 of a
+query row that sees no key at all, a convention the pages leave open ([KB]
+§04 says only that such rows must be handled). Its LSE = -inf is pinned as
+the log-sum-exp of an empty set (scipy), and its zero gradient by finite
+differences of the forward.
 """
 
 from .reference import (  # noqa: F401

@@ -27,7 +27,9 @@ notes of the repository):
 * layout [batch, heads, sequence, head_dim] for every tensor ([KB] §08);
 * LSE uses the natural logarithm;
 * a query row that sees no key has O = 0 and LSE = -inf and passes no
-  gradient (convention; parity unpinned);
+  gradient. LSE = -inf is the log-sum-exp of an empty set; O = 0 is a
+  convention (parity unpinned for that value); given it, the zero gradient
+  follows and is pinned by finite differences;
 * "equivalent" means the same mathematical result, not the same bits
   ([KB] §04), so the comparison with the GPU is tolerance based.
 
@@ -54,9 +56,11 @@ def visible_mask(row_index, nq: int, nkv: int, causal: bool) -> np.ndarray:
 def _softmax_rows(s: np.ndarray):
     """Safe softmax of each row of s (entries may be -inf).
 
-    Returns (P, LSE). A row whose entries are all -inf gets P = 0, LSE = -inf.
+    Returns (P, LSE). A row whose entries are all -inf, or that has no
+    entries at all (no keys), gets P = 0, LSE = -inf: the log-sum-exp of an
+    empty set.
     """
-    m = np.max(s, axis=1, keepdims=True)
+    m = np.max(s, axis=1, keepdims=True, initial=-np.inf)
     empty = ~np.isfinite(m[:, 0])
     m_safe = np.where(np.isfinite(m), m, 0.0)
     e = np.exp(s - m_safe)

@@ -208,9 +208,13 @@ def _loss(q, k, v, do, causal, scale):
     return float(np.sum(o * do))
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_gradients_by_finite_differences(causal):
-    B, Hq, Hkv, nq, nkv, d = 1, 2, 1, 5, 7, 3
+@pytest.mark.parametrize("causal,nq,nkv", [(False, 5, 7), (True, 5, 7), (True, 7, 4)])
+def test_gradients_by_finite_differences(causal, nq, nkv):
+    """Central differences of the forward's loss. The causal 7 x 4 case has
+    query rows 0..2 that see no key: their O is the constant 0 of the no-key
+    convention, so the differences give them zero gradient, and the
+    backward must agree (dQ rows 0..2 are 0 and they add nothing to dK, dV)."""
+    B, Hq, Hkv, d = 1, 2, 1, 3
     q, k, v, do = rnd((B, Hq, nq, d), 35), rnd((B, Hkv, nkv, d), 36), rnd((B, Hkv, nkv, d), 37), rnd((B, Hq, nq, d), 38)
     scale = 0.8
     grads = oracle.attention_backward(q, k, v, do, causal, scale)
@@ -228,6 +232,28 @@ def test_gradients_by_finite_differences(causal):
             fd[idx] = (_loss(*plus, do, causal, scale) - _loss(*minus, do, causal, scale)) / (2 * h)
         rel = np.linalg.norm(g - fd) / np.linalg.norm(fd)
         assert rel <= 1e-6, (which, rel)
+        if which == 0 and causal and nq > nkv:
+            assert np.all(g[:, :, : nq - nkv] == 0) and np.all(np.abs(fd[:, :, : nq - nkv]) < 1e-9)
+
+
+@pytest.mark.parametrize("causal,nq,nkv", [(False, 6, 9), (True, 6, 9), (True, 9, 4), (True, 3, 0)])
+def test_lse_is_scipy_logsumexp_of_the_visible_scores(causal, nq, nkv):
+    """LSE_i is the log-sum-exp of row i's visible scaled scores, as
+    scipy.special.logsumexp computes it (an independent routine); for a row
+    that sees no key that is the log-sum-exp of an empty set, -inf."""
+    from scipy.special import logsumexp
+
+    q, k = rnd((nq, 5), 61), rnd((nkv, 5), 62)
+    scale = 0.6
+    _, lse = oracle.head_forward(q, k, rnd((nkv, 5), 63), causal, scale)
+    vis = oracle.visible_mask(np.arange(nq), nq, nkv, causal)
+    s = scale * (q @ k.T)
+    for i in range(nq):
+        want = logsumexp(s[i, vis[i]]) if vis[i].any() else logsumexp(np.array([]))
+        if np.isneginf(want):
+            assert np.isneginf(lse[i])
+        else:
+            assert lse[i] == pytest.approx(want, abs=1e-12)
 
 
 def test_backward_hand_example_closed_form():

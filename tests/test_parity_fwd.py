@@ -191,6 +191,8 @@ def test_no_keys(dtype):
     o, lse = run_forward(q, k, v, False, 0.125)
     assert torch.all(o == 0)
     assert torch.all(torch.isneginf(lse))
+    o_ref, lse_ref = oracle.attention_forward(to_f64(q), to_f64(k), to_f64(v), False, 0.125)
+    assert np.all(o_ref == 0) and np.all(np.isneginf(lse_ref))
 
 
 def test_gqa_equals_repeated_mha_bitwise():
