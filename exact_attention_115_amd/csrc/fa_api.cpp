@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -18,6 +20,20 @@ bool valid_dtype(int dt) { return dt == FA_F32 || dt == FA_F16 || dt == FA_BF16;
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Whether the product of non-negative factors is below `limit` (> 0). It
+// multiplies factor by factor and stops before a partial product could pass
+// the limit, so sizes near INT_MAX in every argument cannot overflow it.
+bool product_below(std::initializer_list<long long> factors, long long limit) {
+  for (long long f : factors)
+    if (f == 0) return true;
+  long long p = 1;
+  for (long long f : factors) {
+    if (p > (limit - 1) / f) return false;
+    p *= f;
+  }
+  return true;
+}
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -46,8 +62,9 @@ int check_shape(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int dt, bool* em
   }
   // Element counts must fit the kernels' 64-bit offsets and 32-bit grids.
   const long long big = 1LL << 31;
-  if ((long long)B * Hq * (((long long)Nq + 127) / 128) >= big) return FA_ERR_UNSUPPORTED;
-  if ((long long)B * Hq * Nq >= big || (long long)B * Hkv * Nkv >= big) return FA_ERR_UNSUPPORTED;
+  if (!product_below({B, Hq, ((long long)Nq + 127) / 128}, big)) return FA_ERR_UNSUPPORTED;
+  if (!product_below({B, Hq, Nq}, big) || !product_below({B, Hkv, Nkv}, big))
+    return FA_ERR_UNSUPPORTED;
   // One head's K (or V) is addressed with 32-bit byte offsets.
   if ((long long)Nkv * d * 4 >= big) return FA_ERR_UNSUPPORTED;
   *empty = (B == 0 || Hq == 0 || Nq == 0);
@@ -285,7 +302,7 @@ static int check_paged_shape(int B, int Hq, int Hkv, int num_pages, int page_siz
   if (st != FA_OK) return st;
   // One page of one kv head is addressed with 32-bit byte offsets; pages with
   // 64-bit ones.
-  if ((long long)num_pages * Hkv * page_size >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  if (!product_below({num_pages, Hkv, page_size}, 1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -463,7 +480,7 @@ int fa_dropout_mask(unsigned char* keep, int B, int Hq, int Nq, int Nkv, float d
   DropParams dp;
   int st = drop_params(dropout_p, seed, offset, &dp);
   if (st != FA_OK) return st;
-  if ((long long)B * Hq * Nq * Nkv == 0) return FA_OK;
+  if (B == 0 || Hq == 0 || Nq == 0 || Nkv == 0) return FA_OK;
   if ((long long)B * Hq >= (1LL << 31) || (double)B * Hq * Nq * Nkv >= 4.0e18)
     return FA_ERR_UNSUPPORTED;
   if (!keep) return FA_ERR_NULLPTR;

@@ -139,6 +139,36 @@ def test_size_limits_are_enforced():
     assert bwd(B=1, Hq=2, Hkv=2, Nq=1 << 30) == -3
 
 
+def test_extreme_sizes_are_refused_without_overflow():
+    """Sizes near INT_MAX in every argument: the size checks must refuse
+    them without overflowing their own arithmetic (the sanitized replay of
+    this module turns any signed overflow into a failure)."""
+    M = (1 << 31) - 1
+    lib_ = lib()
+    for B, Hq, Hkv, Nq, Nkv in [(M, M, 1, M, 1), (M, M, M, M, M), (1, M, 1, M, M), (M, 1, 1, 1, M),
+                                (M, M, 1, 1, 1)]:
+        for d in (64, 128):
+            assert fwd(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, d=d) == -3, (B, Hq, Hkv, Nq, Nkv, d)
+            assert fwd(B=B, Hq=Hq, Hkv=Hkv, Nq=1, Nkv=Nkv, d=d, ws=P(10),
+                       ws_bytes=1 << 40) in (-3, 0), (B, Hq, Hkv, Nkv, d)
+            assert bwd(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nkv=Nkv, d=d) == -3, (B, Hq, Hkv, Nq, Nkv, d)
+            for dt in (fa.FA_BF16, fa.FA_F32):
+                assert lib_.fa_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, dt) == 0
+                assert lib_.fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, d, dt) == 0
+            assert lib_.fa_fwd_paged_workspace_size(B, Hq, Hkv, 64 * (M // 64), M, d,
+                                                    fa.FA_BF16) == 0
+            assert paged(B=B, Hq=Hq, Hkv=Hkv, num_pages=M, page_size=64 * (M // 64),
+                         max_pages=M, d=d) == -3
+    assert lib_.fa_dropout_mask(P(1), M, M, M, M, 0.5, 1, 0, None) == -3
+    assert fwd_drop(B=M, Hq=M, Hkv=1, Nq=M, Nkv=M) == -3
+    assert bwd_noalloc(B=M, Hq=M, Hkv=1, Nq=M, Nkv=M) == -3
+    assert lib_.fa_bwd_dropout(P(1), P(2), P(3), P(4), P(5), P(6), P(7), P(8), P(9), P(10),
+                               1 << 40, M, M, 1, M, M, 64, 0.125, 0, 0.1, 7, 0, fa.FA_BF16,
+                               None) == -3
+    assert lib_.fa_fwd_fp8(P(1), P(2), P(3), P(4), P(5), M, M, 1, M, M, 128, 0.1, 0, 1.0, 1.0,
+                           1.0, None) == -3
+
+
 def test_fwd_decode_needs_workspace():
     assert fwd(Nq=1, Nkv=8192, ws=None) == -1
     need = lib().fa_fwd_workspace_size(1, 2, 2, 1, 8192, 64, fa.FA_BF16)

@@ -34,6 +34,7 @@ from tests.test_abi import (  # noqa: F401
     test_bwd_noalloc_rejects_bad_arguments_before_any_hip_call,
     test_bwd_rejects_bad_arguments,
     test_dropout_mask_rejects_bad_arguments,
+    test_extreme_sizes_are_refused_without_overflow,
     test_fwd_decode_needs_workspace,
     test_fwd_dropout_rejects_bad_arguments,
     test_fwd_empty_problems_are_noops,
