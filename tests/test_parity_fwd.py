@@ -13,7 +13,7 @@ import torch
 import exact_attention_115_amd as fa
 import oracle
 from synth import WORKLOADS, make_inputs, random_tensors, to_f64
-from tests.parity_util import (TOL, all_finite, check_forward, forward_nan_filled, gpu,
+from tests.parity_util import (all_finite, check_forward, forward_nan_filled, gpu,
                                oracle_heads_forward, run_forward, sample_heads, say)
 
 pytestmark = [
