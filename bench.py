@@ -28,11 +28,13 @@ settle time and the number of steps it ran are reported in the JSON line.
 
 Timing: the K timed steps run back to back between two events (no event
 between kernels), bracketed by synchronizations; ``ms_per_step`` and
-``value`` come from that region. A second region of K steps, right after it,
-records an event after every kernel and gives each kernel's average launch
-duration (``kernel_ms``, the roofline objects). Event records between
-kernels add a few microseconds each, so they are kept out of the step time.
-Decode workloads time each call between its own events instead (see below).
+``value`` come from that region. Then each kernel runs K times back to back
+between two events of its own: its mean launch duration (``kernel_ms``, the
+roofline objects). Last, K steps with an event after every kernel give each
+kernel's median and minimum launch time (``kernel_ms_median``,
+``kernel_ms_min``). Event records between kernels add a few microseconds
+each, so they are kept out of the step time and the means. Decode workloads
+time each call between its own events instead (see below).
 
 Prints ONE JSON line. ``--workload`` selects another synthetic workload for
 development measurements (decode workloads report HBM GB/s, each timed call
@@ -313,47 +315,46 @@ def main():
         names = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if bwd else [])
     seed = 1234
 
+    def check(st, where):
+        if st != 0:
+            raise fa.FAError(st, where)
+
+    # The step's parts, in order, one per entry of `names`: each part is one
+    # kernel launch, or one library call where a call runs several kernels.
+    if fp8:
+        parts = [lambda: check(fa.fa_fwd_fp8(q8, k8, v8, o, lse, w.scale, w.causal, 1.0, 1.0, 1.0,
+                                             stream), "fa_fwd_fp8")]
+    elif drop:
+        parts = [lambda: check(fa.fa_fwd_dropout(q, k, v, o, lse, fwd_ws, w.scale, w.causal,
+                                                 args.dropout, seed, 0, stream), "fa_fwd_dropout")]
+        if bwd:
+            parts.append(lambda: check(fa.fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, bwd_ws,
+                                                         w.scale, w.causal, args.dropout, seed, 0,
+                                                         stream), "fa_bwd_dropout"))
+    else:
+        if paged:
+            parts = [lambda: check(fa.fa_fwd_paged(q, k_pool, v_pool, table, lens, o, lse, fwd_ws,
+                                                   w.scale, stream), "fa_fwd_paged")]
+        else:
+            parts = [lambda: check(fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream),
+                                   "fa_fwd")]
+
+        def stages(*ids):
+            for s_ in ids:
+                check(fa.fa_bwd_stage(s_, q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale,
+                                      w.causal, stream), f"fa_bwd_stage {s_}")
+
+        if bwd:
+            parts += [lambda: stages(0), lambda: stages(1, 2)]
+    assert len(parts) == len(names)
+
     def step(events=None):
         if events is not None:
             events[0].record(stream)
-        if fp8:
-            st = fa.fa_fwd_fp8(q8, k8, v8, o, lse, w.scale, w.causal, 1.0, 1.0, 1.0, stream)
-            if st != 0:
-                raise fa.FAError(st, "fa_fwd_fp8")
+        for j, part in enumerate(parts):
+            part()
             if events is not None:
-                events[1].record(stream)
-            return
-        if drop:
-            st = fa.fa_fwd_dropout(q, k, v, o, lse, fwd_ws, w.scale, w.causal, args.dropout, seed,
-                                   0, stream)
-            if st != 0:
-                raise fa.FAError(st, "fa_fwd_dropout")
-            if events is not None:
-                events[1].record(stream)
-            if bwd:
-                st = fa.fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale, w.causal,
-                                       args.dropout, seed, 0, stream)
-                if st != 0:
-                    raise fa.FAError(st, "fa_bwd_dropout")
-                if events is not None:
-                    events[2].record(stream)
-            return
-        if paged:
-            st = fa.fa_fwd_paged(q, k_pool, v_pool, table, lens, o, lse, fwd_ws, w.scale, stream)
-        else:
-            st = fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream)
-        if st != 0:
-            raise fa.FAError(st, "fa_fwd")
-        if events is not None:
-            events[1].record(stream)
-        if bwd:
-            for s in range(3):
-                st = fa.fa_bwd_stage(s, q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale,
-                                     w.causal, stream)
-                if st != 0:
-                    raise fa.FAError(st, f"fa_bwd_stage {s}")
-                if events is not None and s != 1:
-                    events[2 + s // 2].record(stream)
+                events[j + 1].record(stream)
 
     settle_steps = 0
     if args.settle_ms > 0:
@@ -389,14 +390,27 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+    per_kernel_ms = {}
     if not cold:
-        # Per-kernel durations: a second region of K steps with an event
-        # after every kernel.
+        if w.Nq > 1:
+            # Each kernel's mean launch duration: K launches of that kernel
+            # alone, back to back between two events.
+            for j, n in enumerate(names):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.steps):
+                    parts[j]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per_kernel_ms[n] = e0.elapsed_time(e1) / args.steps
+        # Median and minimum per launch: K steps with an event after every
+        # kernel (the event records add a few microseconds to each).
         for i in range(args.steps):
             step(evs[i])
         torch.cuda.synchronize()
     per_call = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
-    per_kernel_ms = {n: sum(t) / args.steps for n, t in per_call.items()}
+    for n, t in per_call.items():
+        per_kernel_ms.setdefault(n, sum(t) / args.steps)
     if w.Nq == 1:
         # Decode: time per call between its own events. From cold caches the
         # flushes are not counted; with warm caches a call (about 20 us at
