@@ -315,37 +315,58 @@ def main():
         names = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if bwd else [])
     seed = 1234
 
-    def check(st, where):
-        if st != 0:
-            raise fa.FAError(st, where)
-
     # The step's parts, in order, one per entry of `names`: each part is one
     # kernel launch, or one library call where a call runs several kernels.
+    # The parts call the C entry points with their arguments marshalled once
+    # (device pointers, sizes, the stream), so that the Python binding's
+    # per-call checks add no host time between launches; the library still
+    # checks every call's arguments on the host.
+    import ctypes
+
+    lib = fa.load()
+    S = ctypes.c_void_p(stream.cuda_stream)
+
+    def ptr(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def nbytes(t):
+        return 0 if t is None else t.numel() * t.element_size()
+
+    def raw(fn, *a):
+        f = getattr(lib, fn)
+
+        def call():
+            st = f(*a)
+            if st != 0:
+                raise fa.FAError(st, fn)
+        return call
+
+    dt = {torch.float32: fa.FA_F32, torch.float16: fa.FA_F16, torch.bfloat16: fa.FA_BF16}[q.dtype]
+    shape = (w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d)
+    sc, cz = float(w.scale), int(bool(w.causal))
     if fp8:
-        parts = [lambda: check(fa.fa_fwd_fp8(q8, k8, v8, o, lse, w.scale, w.causal, 1.0, 1.0, 1.0,
-                                             stream), "fa_fwd_fp8")]
+        parts = [raw("fa_fwd_fp8", ptr(q8), ptr(k8), ptr(v8), ptr(o), ptr(lse), *shape, sc, cz,
+                     1.0, 1.0, 1.0, S)]
     elif drop:
-        parts = [lambda: check(fa.fa_fwd_dropout(q, k, v, o, lse, fwd_ws, w.scale, w.causal,
-                                                 args.dropout, seed, 0, stream), "fa_fwd_dropout")]
+        parts = [raw("fa_fwd_dropout", ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(fwd_ws),
+                     nbytes(fwd_ws), *shape, sc, cz, args.dropout, seed, 0, dt, S)]
         if bwd:
-            parts.append(lambda: check(fa.fa_bwd_dropout(q, k, v, o, lse, do, dq, dk, dv, bwd_ws,
-                                                         w.scale, w.causal, args.dropout, seed, 0,
-                                                         stream), "fa_bwd_dropout"))
+            parts.append(raw("fa_bwd_dropout", ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(do),
+                             ptr(dq), ptr(dk), ptr(dv), ptr(bwd_ws), nbytes(bwd_ws), *shape, sc,
+                             cz, args.dropout, seed, 0, dt, S))
     else:
         if paged:
-            parts = [lambda: check(fa.fa_fwd_paged(q, k_pool, v_pool, table, lens, o, lse, fwd_ws,
-                                                   w.scale, stream), "fa_fwd_paged")]
+            parts = [raw("fa_fwd_paged", ptr(q), ptr(k_pool), ptr(v_pool), ptr(table), ptr(lens),
+                         ptr(o), ptr(lse), ptr(fwd_ws), nbytes(fwd_ws), w.B, w.Hq, w.Hkv,
+                         k_pool.shape[0], k_pool.shape[2], table.shape[1], w.d, sc, dt, S)]
         else:
-            parts = [lambda: check(fa.fa_fwd(q, k, v, o, lse, fwd_ws, w.scale, w.causal, stream),
-                                   "fa_fwd")]
-
-        def stages(*ids):
-            for s_ in ids:
-                check(fa.fa_bwd_stage(s_, q, k, v, o, lse, do, dq, dk, dv, bwd_ws, w.scale,
-                                      w.causal, stream), f"fa_bwd_stage {s_}")
-
+            parts = [raw("fa_fwd", ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(fwd_ws),
+                         nbytes(fwd_ws), *shape, sc, cz, dt, S)]
         if bwd:
-            parts += [lambda: stages(0), lambda: stages(1, 2)]
+            stage = [raw("fa_bwd_stage", s_, ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(do),
+                         ptr(dq), ptr(dk), ptr(dv), ptr(bwd_ws), nbytes(bwd_ws), *shape, sc, cz,
+                         dt, S) for s_ in range(3)]
+            parts += [stage[0], lambda: (stage[1](), stage[2]())]
     assert len(parts) == len(names)
 
     def step(events=None):
